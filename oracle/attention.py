@@ -1,0 +1,466 @@
+"""Tiled 4-bit attention forward with P-Reordering (oracle; test infrastructure only).
+
+What the pages fix ([HiFA4] Abstract; Section 1):
+* QK^T and PV are both 4-bit GEMMs inside a FlashAttention-style tile loop;
+* the online-softmax state -- running max m, normalizer l, rescaled output
+  O -- is kept in FP16;
+* P-Reordering: l is accumulated from the same quantized weights P-hat that
+  enter the PV product, not from a higher-precision reconstruction of P, so l
+  can be produced by the PV matrix product itself;
+* Theorem 1 (statement only): the conventional ("inconsistent") formulation,
+  l from the higher-precision P but O from P-hat V, scales every channel of a
+  row by the same factor, a net probability-mass loss measured as
+  epsilon = sum(P-hat)/sum(P) - 1 per tile.
+
+Readings where the pages are silent (each is listed in the design notes):
+* scores are kept in the log2 domain: u = S * C with C = fp32(log2(e)/sqrt(d));
+* m is the running max of ceil(fp32(max_tile S * C)), an integer, so the
+  rescale alpha = 2**(m_old - m_new) is exact and m is exact in FP16;
+* P-tilde = X(fma32(S, C, -m)) where X(w) = 2**floor(w) * g(fract(w)) and g is
+  the cubic with g(0) = 1 that passes through the three E2M1 rounding
+  midpoints 1.25, 1.5, 1.75 at log2 of those values.  The 4-bit decision on
+  P-tilde therefore equals round-to-nearest of the true 2**w except within
+  ~1e-7 (relative) of a midpoint, and both sides take it in the same FP32
+  arithmetic (the decision idea follows the FP4 attention prior art [FA4P],
+  which maps scores straight to FP4 probabilities);
+* P-hat uses the same block format as Q, K, V: blocks of 32 keys per row; the
+  block exponent comes from X at the block's largest score;
+* inside a scaled matrix instruction the four 32-element block products are
+  each exact and are added to the accumulator in block order, with one FP32
+  round-to-nearest-even per addition (``mfma_seq``);
+* O_new = fp16(fma32(alpha, O, PV)), l_new = fp16(fma32(alpha, l, L)) with PV
+  and L = rowsum(P-hat) from the same instruction sequence (ones column);
+  out = fp16(fp32(O) / fp32(l));
+* the inconsistent variant sums P-tilde in FP32 in a fixed tree order
+  (pairs (k, k+16), (k, k+8), ... inside each 32-key block, then
+  (s0 + s1) + (s2 + s3) over the blocks of a 128-key tile);
+* causal masking is bottom-right aligned: key c is visible to query r iff
+  c <= r + (Lk - Lq);
+* split-KV decode: splits cover whole tiles, each split runs the recurrence
+  from the empty state, and the FP16 partial states are merged in split order.
+
+Level "P" (parity) is what the GPU is compared against.  Level "S" (semantic)
+rounds only where a narrow format is stored (4-bit codes, FP16 state) and uses
+the true exp2; with the identity quantizer and no FP16 rounding it reduces to
+textbook softmax attention.
+"""
+
+import math
+import numpy as np
+
+from . import fp, mx
+
+F32 = np.float32
+F64 = np.float64
+P_REORDERED = 0
+INCONSISTENT = 1
+
+
+def softmax_scale_log2(d):
+    """C = fp32(log2(e) / sqrt(d)): scores times C are in the log2 domain."""
+    return F32(math.log2(math.e) / math.sqrt(d))
+
+
+def _exp2_cubic():
+    """Coefficients of g(t) = 1 + c1 t + c2 t^2 + c3 t^3 with g(log2 v) = v for v in {1.25, 1.5, 1.75}."""
+    t = np.log2(np.array([1.25, 1.5, 1.75], dtype=F64))
+    a = np.stack([t, t * t, t * t * t], axis=1)
+    c = np.linalg.solve(a, np.array([0.25, 0.5, 0.75], dtype=F64))
+    return F32(c[0]), F32(c[1]), F32(c[2])
+
+
+EXP2_C1, EXP2_C2, EXP2_C3 = _exp2_cubic()
+
+
+def exp2_x(w):
+    """X(w) = ldexp(g(fract(w)), floor(w)) evaluated in FP32 (Horner, one rounding per fma)."""
+    w = np.asarray(w, dtype=F32)
+    n = fp.floor_i32(w)
+    f = fp.fract32(w)
+    g = fp.fma32(fp.fma32(fp.fma32(EXP2_C3, f, EXP2_C2), f, EXP2_C1), f, F32(1.0))
+    return fp.ldexp32(g, n)
+
+
+def mfma_seq(blocks, acc=None):
+    """Scaled-MFMA accumulation model.
+
+    ``blocks`` are exact FP64 block products (sum over 32 elements of
+    value(a) * value(b), times both block scales).  They are added to the
+    accumulator in order with one FP32 RNE rounding each.  Returns the FP32
+    result and a mask of elements whose every partial sum was exactly
+    representable (there the result is the exact sum, whatever the adder does).
+    """
+    shape = np.broadcast_shapes(*[np.shape(b) for b in blocks])
+    a = np.zeros(shape, dtype=F64) if acc is None else np.broadcast_to(np.asarray(acc, dtype=F32).astype(F64), shape).copy()
+    exact = np.ones(shape, dtype=bool)
+    for b in blocks:
+        b = np.broadcast_to(np.asarray(b, dtype=F64), shape)
+        s = a + b
+        bb = s - a
+        err = (a - (s - bb)) + (b - bb)
+        r = fp.rn32_sum(a, b).astype(F64)
+        exact &= (err == 0) & (r == s)
+        a = r
+    return a.astype(F32), exact
+
+
+# ----------------------------------------------------------------------------------------------
+# quantized operands
+# ----------------------------------------------------------------------------------------------
+
+class Quantized:
+    """Unpacked codes and block exponents of Q-hat, K-hat, V-hat.
+
+    qc [B, Hq, Lq, d], qe [B, Hq, Lq, d/32]; kc [B, Hkv, Lk, d], ke [B, Hkv, Lk, d/32];
+    vc [B, Hkv, d, Lk32], ve [B, Hkv, d, Lk32/32] with Lk32 = Lk rounded up to 32
+    (V-hat is blocked along tokens; tokens past Lk are zero).
+    """
+
+    def __init__(self, qc, qe, kc, ke, vc, ve, lk):
+        self.qc, self.qe, self.kc, self.ke, self.vc, self.ve = qc, qe, kc, ke, vc, ve
+        self.lk = lk
+
+    def packed(self):
+        """Bytes in the library's HBM layout: (q_codes, q_scales, k_codes, k_scales, v_codes, v_scales)."""
+        return (mx.pack_codes(self.qc), mx.scale_bytes(self.qe), mx.pack_codes(self.kc),
+                mx.scale_bytes(self.ke), mx.pack_codes(self.vc), mx.scale_bytes(self.ve))
+
+
+def quantize_qkv(q, k, v, s32=None, inv32=None):
+    """Smooth-QK (if scales given) then 4-bit block quantization.
+
+    q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d] hold FP16 values.  Q and K are
+    blocked along d, V along tokens.
+    """
+    from . import smooth
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    b, hq, lq, d = q.shape
+    hkv, lk = k.shape[1], k.shape[2]
+    group = hq // hkv
+    if s32 is not None:
+        qs = smooth.apply(q, s32, np.arange(hq) // group)
+        ks = smooth.apply(k, inv32, np.arange(hkv))
+    else:
+        qs = q.astype(F32)
+        ks = k.astype(F32)
+    qc, qe = mx.quantize_blocks(qs.astype(F64))
+    kc, ke = mx.quantize_blocks(ks.astype(F64))
+    lk32 = -(-lk // 32) * 32
+    vt = np.zeros((b, hkv, d, lk32), dtype=F64)
+    vt[..., :lk] = np.swapaxes(v.astype(F64), 2, 3)
+    vc, ve = mx.quantize_blocks(vt)
+    return Quantized(qc, qe, kc, ke, vc, ve, lk)
+
+
+# ----------------------------------------------------------------------------------------------
+# scores
+# ----------------------------------------------------------------------------------------------
+
+def scores_p(qc, qe, kc, ke):
+    """S_raw = Q-hat K-hat^T as the matrix instruction computes it (Level P).
+
+    Returns (S fp32 [R, N], exact mask).  Blocks run along d in order.
+    """
+    d = qc.shape[-1]
+    qh = mx.code_half_units(qc)
+    kh = mx.code_half_units(kc)
+    blocks = []
+    for j in range(d // 32):
+        sl = slice(32 * j, 32 * j + 32)
+        i = qh[:, sl] @ kh[:, sl].T  # exact integers, units of 1/4
+        e = qe[:, j][:, None] + ke[:, j][None, :] - 2
+        blocks.append(i.astype(F64) * np.exp2(e.astype(F64)))
+    return mfma_seq(blocks)
+
+
+def scores_exact(qv, kv):
+    """S = Q K^T in FP64 from dequantized (or unquantized) values (Level S)."""
+    return np.asarray(qv, dtype=F64) @ np.asarray(kv, dtype=F64).T
+
+
+def visibility(rows, lq, lk, n_pad, causal):
+    """Boolean [R, n_pad]: key c visible to query r."""
+    c = np.arange(n_pad)[None, :]
+    r = np.asarray(rows)[:, None]
+    vis = np.broadcast_to(c < lk, (len(rows), n_pad))
+    if causal:
+        vis = vis & (c <= r + (lk - lq))
+    return np.array(vis)
+
+
+def _tree_sum32(x):
+    """FP32 sum of the last axis (length 32) in the kernel's pairwise order."""
+    t = np.asarray(x, dtype=F32)
+    while t.shape[-1] > 1:
+        h = t.shape[-1] // 2
+        t = fp.add32(t[..., :h], t[..., h:])
+    return t[..., 0]
+
+
+# ----------------------------------------------------------------------------------------------
+# the recurrence
+# ----------------------------------------------------------------------------------------------
+
+class State:
+    def __init__(self, m, l, o):
+        self.m, self.l, self.o = m, l, o
+
+
+class Diag:
+    """Diagnostics: counts of sums that are not exactly representable, epsilon tiles."""
+
+    def __init__(self):
+        self.inexact_s = 0
+        self.inexact_pv = 0
+        self.inexact_l = 0
+        self.total_s = 0
+        self.total_pv = 0
+        self.stats = []  # (row_block, tile, sum_phat, sum_p)
+
+
+def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row_ids=None):
+    """Level-P tile loop for one head over tiles [tile_lo, tile_hi).
+
+    s fp32 [R, Npad] scores, vis [R, Npad], vh int64 [d, Npad] V-hat codes in
+    half units, ve int64 [d, Npad/32] V-hat block exponents.  Returns the FP16
+    state (m as FP32 integer values, l, O as FP16).
+    """
+    r_n = s.shape[0]
+    d = vh.shape[0]
+    m = np.full(r_n, -np.inf, dtype=F32)
+    l16 = np.zeros(r_n, dtype=np.float16)
+    o16 = np.zeros((r_n, d), dtype=np.float16)
+    nb = bc // 32
+    for t in range(tile_lo, tile_hi):
+        k0 = t * bc
+        st = s[:, k0:k0 + bc]
+        vt = vis[:, k0:k0 + bc]
+        anyv = vt.any(axis=1)
+        smax = np.where(vt, st, F32(-np.inf)).max(axis=1).astype(F32)
+        with np.errstate(invalid="ignore"):
+            tm = np.ceil(fp.mul32(smax, c32)).astype(F32)
+        m_new = np.where(anyv, np.maximum(m, tm), m).astype(F32)
+        with np.errstate(invalid="ignore", over="ignore"):
+            alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2((m - m_new).astype(F64))))
+        alpha = alpha.astype(F32)
+        mm = np.where(np.isfinite(m_new), m_new, F32(0)).astype(F32)
+        w = fp.fma32(np.where(vt, st, F32(0)), c32, -mm[:, None])
+        ptil = np.where(vt, exp2_x(w), F32(0)).astype(F32)
+        codes = np.zeros(st.shape, dtype=np.uint8)
+        eb = np.full((r_n, nb), -127, dtype=np.int64)
+        for j in range(nb):
+            sl = slice(32 * j, 32 * j + 32)
+            vb = vt[:, sl]
+            has = vb.any(axis=1)
+            bmax = np.where(vb, st[:, sl], F32(-np.inf)).max(axis=1)
+            bmax = np.where(has, bmax, F32(0)).astype(F32)
+            xb = exp2_x(fp.fma32(bmax, c32, -mm))
+            e = np.where(has, mx.scale_exponent(xb), -127)
+            eb[:, j] = e
+            y = ptil[:, sl].astype(F64) * np.exp2(-e.astype(F64))[:, None]
+            codes[:, sl] = np.where(vb, mx.rne_code(y), 0)
+        ph = mx.code_half_units(codes)
+        pv_blocks = []
+        l_blocks = []
+        for j in range(nb):
+            kb = k0 + 32 * j
+            sl = slice(32 * j, 32 * j + 32)
+            i = ph[:, sl] @ vh[:, kb:kb + 32].T
+            e = eb[:, j][:, None] + ve[:, kb // 32][None, :] - 2
+            pv_blocks.append(i.astype(F64) * np.exp2(e.astype(F64)))
+            i1 = ph[:, sl].sum(axis=1) * 2  # times the ones column (value 1 = 2 half units)
+            l_blocks.append(i1.astype(F64) * np.exp2((eb[:, j] - 2).astype(F64)))
+        pv, ok_pv = mfma_seq(pv_blocks)
+        lsum, ok_l = mfma_seq(l_blocks)
+        if mode == INCONSISTENT:
+            sums = [_tree_sum32(ptil[:, 32 * j:32 * j + 32]) for j in range(nb)]
+            sums += [np.zeros(r_n, dtype=F32)] * (4 - nb) if nb < 4 else []
+            lsum = fp.add32(fp.add32(sums[0], sums[1]), fp.add32(sums[2], sums[3]))
+        o16 = fp.rn16(fp.fma32(alpha[:, None], o16.astype(F32), pv))
+        l16 = fp.rn16(fp.fma32(alpha, l16.astype(F32), lsum))
+        m = m_new
+        if diag is not None:
+            rows_touch = anyv
+            diag.inexact_pv += int((~ok_pv[rows_touch]).sum())
+            diag.inexact_l += int((~ok_l[rows_touch]).sum())
+            diag.total_pv += int(rows_touch.sum()) * d
+            if row_ids is not None:
+                phat = mx.code_value(codes) * np.exp2(np.repeat(eb, 32, axis=1).astype(F64))
+                for rb in np.unique(np.asarray(row_ids) // 32):
+                    sel = (np.asarray(row_ids) // 32) == rb
+                    if vt[sel].any():
+                        diag.stats.append((int(rb), t, float(phat[sel].sum()), float(ptil[sel].astype(F64).sum())))
+    return State(m, l16, o16)
+
+
+def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True, round_state=True):
+    """Level-S tile loop: exact scores and exp2, rounding only where a narrow format is stored.
+
+    vvals FP64 [Npad, d] (dequantized V-hat, or the raw V for the identity quantizer).
+    """
+    r_n = s64.shape[0]
+    d = vvals.shape[1]
+    m = np.full(r_n, -np.inf)
+    l = np.zeros(r_n)
+    o = np.zeros((r_n, d))
+    nb = bc // 32
+    for t in range(tile_lo, tile_hi):
+        k0 = t * bc
+        st = s64[:, k0:k0 + bc]
+        vt = vis[:, k0:k0 + bc]
+        anyv = vt.any(axis=1)
+        smax = np.where(vt, st, -np.inf).max(axis=1)
+        with np.errstate(invalid="ignore"):
+            m_new = np.where(anyv, np.maximum(m, np.ceil(smax * c64)), m)
+            alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2(m - m_new)))
+        mm = np.where(np.isfinite(m_new), m_new, 0.0)
+        p = np.where(vt, np.exp2(np.where(vt, st, 0.0) * c64 - mm[:, None]), 0.0)
+        if quantize:
+            ph = np.zeros_like(p)
+            for j in range(nb):
+                sl = slice(32 * j, 32 * j + 32)
+                e = mx.scale_exponent(p[:, sl].max(axis=1))
+                y = p[:, sl] * np.exp2(-e.astype(F64))[:, None]
+                ph[:, sl] = mx.code_value(mx.rne_code(y)) * np.exp2(e.astype(F64))[:, None]
+        else:
+            ph = p
+        pv = ph @ vvals[k0:k0 + bc]
+        lsum = (p if mode == INCONSISTENT else ph).sum(axis=1)
+        o = alpha[:, None] * o + pv
+        l = alpha * l + lsum
+        if round_state:
+            o = o.astype(np.float16).astype(F64)
+            l = l.astype(np.float16).astype(F64)
+        m = m_new
+    return State(m, l, o)
+
+
+def finish(state, level="P"):
+    """out = fp16(fp32(O) / fp32(l)) (Level P) or O / l rounded once to FP16 (Level S)."""
+    if level == "P":
+        return fp.rn16(fp.div32(state.o.astype(F32), state.l.astype(F32)[:, None]))
+    return (state.o / state.l[:, None]).astype(np.float16)
+
+
+def merge_splits(states):
+    """Merge FP16 split states in split order (Level P)."""
+    r_n, d = states[0].o.shape
+    m = np.full(r_n, -np.inf, dtype=F32)
+    l = np.zeros(r_n, dtype=np.float16)
+    o = np.zeros((r_n, d), dtype=np.float16)
+    for st in states:
+        ms = st.m.astype(np.float16).astype(F32)  # the partial max is stored in FP16
+        with np.errstate(invalid="ignore"):
+            mn = np.maximum(m, ms)
+        live = np.isfinite(ms)
+        with np.errstate(invalid="ignore", over="ignore"):
+            a1 = np.where(np.isneginf(m), 0.0, np.exp2((m - mn).astype(F64))).astype(F32)
+            a2 = np.where(live, np.exp2(np.where(live, ms - mn, 0).astype(F64)), 0.0).astype(F32)
+        mo = fp.mul32(a2[:, None], st.o.astype(F32))
+        ml = fp.mul32(a2, st.l.astype(F32))
+        o_new = fp.rn16(fp.fma32(a1[:, None], o.astype(F32), mo))
+        l_new = fp.rn16(fp.fma32(a1, l.astype(F32), ml))
+        o = np.where(live[:, None], o_new, o)
+        l = np.where(live, l_new, l)
+        m = np.where(live, mn, m).astype(F32)
+    return State(m, l, o)
+
+
+def split_tiles(n_tiles, num_splits):
+    """Tile ranges of the splits: ceil(n_tiles / S) tiles each, the last ones possibly empty."""
+    per = -(-n_tiles // num_splits)
+    return [(min(s * per, n_tiles), min((s + 1) * per, n_tiles)) for s in range(num_splits)]
+
+
+def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, stats=False):
+    """Level-P output rows of one (batch, query head): FP16 [len(rows), d]."""
+    hq = qq.qc.shape[1]
+    hkv = qq.kc.shape[1]
+    g = h // (hq // hkv)
+    lq = qq.qc.shape[2]
+    lk = qq.lk
+    d = qq.qc.shape[3]
+    rows = np.asarray(rows)
+    s, ok_s = scores_p(qq.qc[b, h, rows], qq.qe[b, h, rows], qq.kc[b, g], qq.ke[b, g])
+    n_tiles = -(-lk // bc)
+    npad = n_tiles * bc
+    s_pad = np.zeros((len(rows), npad), dtype=F32)
+    s_pad[:, :lk] = s
+    vis = visibility(rows, lq, lk, npad, causal)
+    vh = np.zeros((d, npad), dtype=np.int64)
+    lk32 = qq.vc.shape[3]
+    vh[:, :lk32] = mx.code_half_units(qq.vc[b, g])
+    ve = np.full((d, npad // 32), -127, dtype=np.int64)
+    ve[:, :lk32 // 32] = qq.ve[b, g]
+    if diag is not None:
+        diag.inexact_s += int((~ok_s & vis[:, :lk]).sum())
+        diag.total_s += int(vis[:, :lk].sum())
+    c32 = softmax_scale_log2(d)
+    if num_splits <= 1:
+        st = recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, 0, n_tiles, diag, rows if stats else None)
+        return finish(st, "P")
+    states = [recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, lo, hi, diag) for lo, hi in split_tiles(n_tiles, num_splits)]
+    return finish(merge_splits(states), "P")
+
+
+def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None):
+    """Full Level-P output FP16 [B, Hq, Lq, d]."""
+    b_n, hq, lq, d = qq.qc.shape
+    out = np.zeros((b_n, hq, lq, d), dtype=np.float16)
+    for b in range(b_n):
+        for h in range(hq):
+            out[b, h] = attention_head_p(qq, b, h, np.arange(lq), causal, bc, mode, num_splits, diag)
+    return out
+
+
+def tile_stats_p(qq, causal, bc, b, h):
+    """Epsilon statistics of one head: list of (row_block_of_32, tile, sum P-hat, sum P-tilde)."""
+    diag = Diag()
+    lq = qq.qc.shape[2]
+    attention_head_p(qq, b, h, np.arange(lq), causal, bc, P_REORDERED, 1, diag, stats=True)
+    return diag.stats
+
+
+def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_state=True, num_splits=1):
+    """Level-S output for one head from values: qv [Lq, d], kv [Lk, d], vv [Lk, d] (FP64 values).
+
+    With quantize=False and round_state=False this is textbook softmax attention.
+    """
+    lq, d = qv.shape
+    lk = kv.shape[0]
+    n_tiles = -(-lk // bc)
+    npad = n_tiles * bc
+    s = np.zeros((lq, npad))
+    s[:, :lk] = scores_exact(qv, kv)
+    vis = visibility(np.arange(lq), lq, lk, npad, causal)
+    vpad = np.zeros((npad, d))
+    vpad[:lk] = vv
+    c64 = math.log2(math.e) / math.sqrt(d)
+    if num_splits <= 1:
+        st = recurrence_s(s, vis, vpad, c64, bc, mode, 0, n_tiles, quantize, round_state)
+        return st.o / st.l[:, None] if not round_state else finish(st, "S")
+    # split + exact merge (Level S keeps the partials in FP64)
+    parts = [recurrence_s(s, vis, vpad, c64, bc, mode, lo, hi, quantize, round_state)
+             for lo, hi in split_tiles(n_tiles, num_splits) if hi > lo]
+    m = np.max([p.m for p in parts], axis=0)
+    o = sum(np.exp2(p.m - m)[:, None] * p.o for p in parts)
+    l = sum(np.exp2(p.m - m) * p.l for p in parts)
+    return o / l[:, None]
+
+
+def reference_fp32(q, k, v, causal):
+    """Unquantized softmax(Q K^T / sqrt(d) + mask) V computed in FP32 for one head ([L, d] arrays)."""
+    q = np.asarray(q, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    v = np.asarray(v, dtype=F32)
+    lq, d = q.shape
+    lk = k.shape[0]
+    s = (q @ k.T) * F32(1.0 / math.sqrt(d))
+    if causal:
+        vis = visibility(np.arange(lq), lq, lk, lk, True)
+        s = np.where(vis, s, F32(-np.inf))
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
