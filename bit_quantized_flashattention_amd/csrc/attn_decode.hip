@@ -1,0 +1,233 @@
+// K3: split-KV decode (one query token per sequence) and the FP16 (m, l, O) merge, gfx950.
+//
+// Decode is HBM-bound: every K-hat/V-hat byte is used by exactly one MFMA lane once, so the
+// kernel skips LDS and loads each lane's MFMA operands straight from HBM into registers, one
+// tile ahead of the computation.  The query heads of a GQA group are the MFMA columns (the
+// same S^T = K-hat Q-hat^T layout as the prefill kernel, see attn_prefill.hip), so a wave
+// serves one (batch, KV head, split) and keeps its split's FP16 state in registers.
+#include "device_common.h"
+#include "launch.h"
+
+namespace hifa4 {
+
+namespace {
+
+struct TileOps {
+  uint4 k[8][2];      // K-hat A operands of the 8 score MFMAs (2 contraction steps for d = 256)
+  uint32_t ksc[8][2];
+  uint4 v[16];        // V-hat^T A operands of the 16-channel blocks (up to d = 256)
+  uint32_t vsc[16];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileOps& t, const uint8_t* kc, const uint8_t* ks,
+                                          const uint8_t* vc, const uint8_t* vs, int64_t k0,
+                                          int64_t lk, int64_t lk32, int bc, int col, int g) {
+  constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
+#pragma unroll
+  for (int tt = 0; tt < 8; tt++) {
+    const int kr = 32 * (col >> 2) + 4 * tt + (col & 3);
+    const int64_t key = k0 + kr;
+    const bool ok = kr < bc && key < lk && (D >= 128 || g < 2);
+#pragma unroll
+    for (int st = 0; st < KSTEPS; st++) {
+      t.k[tt][st] = ok ? *reinterpret_cast<const uint4*>(kc + key * (D / 2) + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+      t.ksc[tt][st] = ok ? ks[key * (D / kBlock) + 4 * st + g] : 127u;
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < D / 16; cb++) {
+    const int ch = 16 * cb + col;
+    const bool ok = 32 * g < bc && k0 + 32 * g < lk32;
+    t.v[cb] = ok ? *reinterpret_cast<const uint4*>(vc + (int64_t)ch * (lk32 / 2) + k0 / 2 + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+    t.vsc[cb] = ok ? vs[(int64_t)ch * (lk32 / kBlock) + k0 / kBlock + g] : 127u;
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
+  constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
+  constexpr int CB = D / 16;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, col = lane & 15;
+  const int split = blockIdx.x;
+  const int group = a.heads_q / a.heads_kv;
+  const int hchunk = blockIdx.y % ((group + 15) / 16);
+  const int kvh = blockIdx.y / ((group + 15) / 16);
+  const int b = blockIdx.z;
+  const int hl = 16 * hchunk + col;            // query head within the group (MFMA column)
+  const bool live_col = hl < group;
+  const int h = kvh * group + (live_col ? hl : 0);
+  const int64_t lk = a.len_kv, lk32 = a.len_kv32;
+  const int bc = a.kv_tile;
+
+  const int t_lo = split * a.tiles_per_split;
+  int t_hi = t_lo + a.tiles_per_split;
+  if (t_hi > a.n_tiles) t_hi = a.n_tiles;
+
+  // Q-hat^T operand: column = query head, K-chunk g
+  uint4 qreg[KSTEPS];
+  uint32_t qsc[KSTEPS];
+  const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (D / 2);
+  const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (D / kBlock);
+#pragma unroll
+  for (int st = 0; st < KSTEPS; st++) {
+    const bool ok = live_col && (D >= 128 || g < 2);
+    qreg[st] = ok ? *reinterpret_cast<const uint4*>(qc + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+    qsc[st] = ok ? qs[4 * st + g] : 127u;
+  }
+
+  const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);
+  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk * (D / kBlock);
+  const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / 2);
+  const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / kBlock);
+  const float C = a.c_log2;
+  const int64_t shift = lk - 1;
+
+  h2 o[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) o[cb][0] = o[cb][1] = h2{(_Float16)0.0f, (_Float16)0.0f};
+  float l = 0.0f, m = -INFINITY;
+
+  TileOps cur, nxt;
+  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
+  for (int tile = t_lo; tile < t_hi; tile++) {
+    const int64_t k0 = (int64_t)tile * bc;
+    if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, k0 + bc, lk, lk32, bc, col, g);
+    float s[32];
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++) {
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; st++) acc = mfma_fp4(cur.k[tt][st], cur.ksc[tt][st], qreg[st], qsc[st], acc);
+#pragma unroll
+      for (int i = 0; i < 4; i++) s[4 * tt + i] = acc[i];
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      const int64_t key = k0 + 32 * g + k;
+      const bool vis = (32 * g + k < bc) && key < lk && key <= shift && live_col;
+      s[k] = vis ? s[k] : -INFINITY;
+      bmax = fmaxf(bmax, s[k]);
+    }
+    float rmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float m_new = fmaxf(m, __builtin_ceilf(rmax * C));
+    float alpha = 1.0f;
+    if (m_new != m) alpha = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
+    const float negm = (m_new == -INFINITY) ? 0.0f : -m_new;
+    // P-hat: one scale per (query, tile) from the tile's largest score (all four lane groups agree)
+    int e = -127;
+    if (rmax != -INFINITY) e = mx_exponent(exp2_x(__builtin_fmaf(rmax, C, negm), a.c1, a.c2, a.c3));
+    const float scl = e8m0_as_float(e);
+    float p[32];
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      const float x = exp2_x(__builtin_fmaf(s[k], C, negm), a.c1, a.c2, a.c3);
+      p[k] = s[k] == -INFINITY ? 0.0f : x;
+    }
+    uint4 ph;
+    ph.x = pack8_fp4(p + 0, scl);
+    ph.y = pack8_fp4(p + 8, scl);
+    ph.z = pack8_fp4(p + 16, scl);
+    ph.w = pack8_fp4(p + 24, scl);
+    const uint32_t psc = (uint32_t)(e + 127);
+    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+    v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
+    float lsum = lacc[0];
+    if (MODE == 1) {
+      float t16[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) t16[k] = p[k] + p[k + 16];
+#pragma unroll
+      for (int k = 0; k < 8; k++) t16[k] = t16[k] + t16[k + 8];
+#pragma unroll
+      for (int k = 0; k < 4; k++) t16[k] = t16[k] + t16[k + 4];
+#pragma unroll
+      for (int k = 0; k < 2; k++) t16[k] = t16[k] + t16[k + 2];
+      const float sb = t16[0] + t16[1];
+      const float s01 = sb + __shfl_xor(sb, 16);
+      lsum = s01 + __shfl_xor(s01, 32);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
+      pv = mfma_fp4(cur.v[cb], cur.vsc[cb], ph, psc, pv);
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        const float o0 = __builtin_fmaf(alpha, (float)o[cb][hh][0], pv[2 * hh]);
+        const float o1 = __builtin_fmaf(alpha, (float)o[cb][hh][1], pv[2 * hh + 1]);
+        o[cb][hh] = h2{(_Float16)o0, (_Float16)o1};
+      }
+    }
+    l = (float)(_Float16)__builtin_fmaf(alpha, l, lsum);
+    m = m_new;
+    if (tile + 1 < t_hi) cur = nxt;
+  }
+
+  if (!live_col) return;
+  const int64_t part = ((int64_t)b * a.heads_q + h) * a.num_splits + split;
+  uint16_t* po = a.part_o + part * D;
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    uint2 w;
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, o[cb][0][0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[cb][0][1]) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, o[cb][1][0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[cb][1][1]) << 16);
+    *reinterpret_cast<uint2*>(po + 16 * cb + 4 * g) = w;
+  }
+  if (g == 0) {
+    a.part_ml[part * 2 + 0] = __builtin_bit_cast(uint16_t, (_Float16)m);
+    a.part_ml[part * 2 + 1] = __builtin_bit_cast(uint16_t, (_Float16)l);
+  }
+}
+
+// Sequential FP16 merge of the split states, one thread per (batch, head, channel).
+template <int D>
+__global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int ch = threadIdx.x;
+  float m = -INFINITY, l = 0.0f, o = 0.0f;
+  for (int s = 0; s < a.num_splits; s++) {
+    const int64_t part = bh * a.num_splits + s;
+    const float ms = (float)__builtin_bit_cast(_Float16, a.part_ml[part * 2 + 0]);
+    if (!(ms > -INFINITY)) continue;  // the split saw no key
+    const float ls = (float)__builtin_bit_cast(_Float16, a.part_ml[part * 2 + 1]);
+    const float os = (float)__builtin_bit_cast(_Float16, a.part_o[part * D + ch]);
+    const float mn = fmaxf(m, ms);
+    const float a1 = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - mn));
+    const float a2 = __builtin_ldexpf(1.0f, (int)(ms - mn));
+    const float mo = a2 * os;
+    const float ml = a2 * ls;
+    o = (float)(_Float16)__builtin_fmaf(a1, o, mo);
+    l = (float)(_Float16)__builtin_fmaf(a1, l, ml);
+    m = mn;
+  }
+  a.out[bh * D + ch] = __builtin_bit_cast(uint16_t, (_Float16)(o / l));
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  const int group = a.heads_q / a.heads_kv;
+  dim3 grid((uint32_t)a.num_splits, (uint32_t)(a.heads_kv * ((group + 15) / 16)), (uint32_t)a.batch);
+  if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((attn_decode_split_kernel<D, 0>), grid, dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((uint32_t)((int64_t)a.batch * a.heads_q)), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return launch_d<64>(a, s);
+    case 128: return launch_d<128>(a, s);
+    case 256: return launch_d<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hifa4

@@ -1,0 +1,299 @@
+// C ABI of libhifa4: argument validation, host-side Smooth-QK calibration, launch dispatch.
+#include "hifa4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hifa4_status fail(hifa4_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+hifa4_status ok() {
+  g_last_error.clear();
+  return HIFA4_OK;
+}
+
+float half_bits_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const uint32_t ex = (h >> 10) & 0x1F;
+  uint32_t man = h & 0x3FF;
+  uint32_t bits;
+  if (ex == 0) {
+    if (man == 0) {
+      bits = sign;
+    } else {  // subnormal: normalize
+      int e = -1;
+      do {
+        man <<= 1;
+        e++;
+      } while ((man & 0x400) == 0);
+      bits = sign | ((uint32_t)(127 - 15 - e) << 23) | ((man & 0x3FF) << 13);
+    }
+  } else if (ex == 31) {
+    bits = sign | 0x7F800000u | (man << 13);
+  } else {
+    bits = sign | ((ex - 15 + 127) << 23) | (man << 13);
+  }
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+// Coefficients of the cubic g(t) = 1 + c1 t + c2 t^2 + c3 t^3 through the E2M1 rounding
+// midpoints (log2 v, v), v in {1.25, 1.5, 1.75}: Cramer's rule on the 3x3 Vandermonde-like system.
+void exp2_cubic(float* c1, float* c2, float* c3) {
+  const double t[3] = {std::log2(1.25), std::log2(1.5), std::log2(1.75)};
+  const double r[3] = {0.25, 0.5, 0.75};
+  double m[3][3];
+  for (int i = 0; i < 3; i++) {
+    m[i][0] = t[i];
+    m[i][1] = t[i] * t[i];
+    m[i][2] = t[i] * t[i] * t[i];
+  }
+  auto det3 = [](const double a[3][3]) {
+    return a[0][0] * (a[1][1] * a[2][2] - a[1][2] * a[2][1]) -
+           a[0][1] * (a[1][0] * a[2][2] - a[1][2] * a[2][0]) +
+           a[0][2] * (a[1][0] * a[2][1] - a[1][1] * a[2][0]);
+  };
+  const double det = det3(m);
+  double c[3];
+  for (int j = 0; j < 3; j++) {
+    double mj[3][3];
+    for (int i = 0; i < 3; i++)
+      for (int k = 0; k < 3; k++) mj[i][k] = (k == j) ? r[i] : m[i][k];
+    c[j] = det3(mj) / det;
+  }
+  *c1 = (float)c[0];
+  *c2 = (float)c[1];
+  *c3 = (float)c[2];
+}
+
+hifa4_status check_dims(const hifa4_dims* d) {
+  if (d == nullptr) return fail(HIFA4_ERR_NULL, "dims is NULL");
+  if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->len_q < 1 || d->len_kv < 1)
+    return fail(HIFA4_ERR_SHAPE, "batch, heads and lengths must be >= 1");
+  if (d->heads_q % d->heads_kv != 0) return fail(HIFA4_ERR_SHAPE, "heads_q must be a multiple of heads_kv");
+  const int group = d->heads_q / d->heads_kv;
+  if (group > 8 && group % 8 != 0)
+    return fail(HIFA4_ERR_UNSUPPORTED, "heads_q / heads_kv must be <= 8 or a multiple of 8");
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(HIFA4_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (d->len_q > (int64_t)1 << 31 || d->len_kv > (int64_t)1 << 31)
+    return fail(HIFA4_ERR_SHAPE, "lengths must be <= 2^31");
+  return HIFA4_OK;
+}
+
+int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
+
+int32_t auto_splits(const hifa4_dims* d, int kv_tile) {
+  // enough (batch, KV head, split) work-groups to cover the 256 compute units several times,
+  // with at least 8 tiles per split
+  const int64_t tiles = (d->len_kv + kv_tile - 1) / kv_tile;
+  const int64_t units = (int64_t)d->batch * d->heads_kv;
+  int64_t s = (2048 + units - 1) / units;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 8));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, 64));
+  return (int32_t)s;
+}
+
+hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
+  if (o == nullptr) return fail(HIFA4_ERR_NULL, "opts is NULL");
+  if (o->causal != 0 && o->causal != 1) return fail(HIFA4_ERR_SHAPE, "causal must be 0 or 1");
+  if (o->normalizer != HIFA4_P_REORDERED && o->normalizer != HIFA4_INCONSISTENT)
+    return fail(HIFA4_ERR_SHAPE, "normalizer must be HIFA4_P_REORDERED or HIFA4_INCONSISTENT");
+  if (o->kv_tile != 64 && o->kv_tile != 128) return fail(HIFA4_ERR_UNSUPPORTED, "kv_tile must be 64 or 128");
+  if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
+  if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
+  return HIFA4_OK;
+}
+
+int32_t resolve_splits(const hifa4_dims* d, const hifa4_attn_opts* o) {
+  if (d->len_q != 1) return 1;
+  const int64_t tiles = (d->len_kv + o->kv_tile - 1) / o->kv_tile;
+  int64_t s = o->num_splits > 0 ? o->num_splits : auto_splits(d, o->kv_tile);
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, tiles));
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hifa4_status_string(hifa4_status status) {
+  switch (status) {
+    case HIFA4_OK: return "ok";
+    case HIFA4_ERR_NULL: return "null pointer";
+    case HIFA4_ERR_SHAPE: return "invalid shape or argument";
+    case HIFA4_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HIFA4_ERR_WORKSPACE: return "workspace missing or too small";
+    case HIFA4_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* hifa4_last_error(void) { return g_last_error.c_str(); }
+
+hifa4_status hifa4_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64_t n_tokens,
+                             int32_t heads_q, int32_t heads_kv, int32_t head_dim, float alpha,
+                             float gate_tau, float* s, float* inv_s, int32_t* gate_on) {
+  if (!q_cal || !k_cal || !s || !inv_s || !gate_on) return fail(HIFA4_ERR_NULL, "calibrate: NULL argument");
+  if (n_tokens < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || heads_q % heads_kv != 0)
+    return fail(HIFA4_ERR_SHAPE, "calibrate: need n_tokens, heads, head_dim >= 1 and heads_q % heads_kv == 0");
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(HIFA4_ERR_SHAPE, "calibrate: alpha must be in [0, 1]");
+  const int group = heads_q / heads_kv;
+  const int64_t d = head_dim;
+  std::vector<double> aq((size_t)heads_kv * d, 0.0), ak((size_t)heads_kv * d, 0.0);
+  for (int g = 0; g < heads_kv; g++) {
+    for (int64_t t = 0; t < n_tokens; t++) {
+      for (int64_t j = 0; j < d; j++) {
+        const double v = std::fabs((double)half_bits_to_float(k_cal[((int64_t)g * n_tokens + t) * d + j]));
+        double& dst = ak[(size_t)g * d + j];
+        dst = std::max(dst, v);
+      }
+    }
+    for (int hh = 0; hh < group; hh++) {
+      const int h = g * group + hh;
+      for (int64_t t = 0; t < n_tokens; t++) {
+        for (int64_t j = 0; j < d; j++) {
+          const double v = std::fabs((double)half_bits_to_float(q_cal[((int64_t)h * n_tokens + t) * d + j]));
+          double& dst = aq[(size_t)g * d + j];
+          dst = std::max(dst, v);
+        }
+      }
+    }
+  }
+  std::vector<double> sorted = ak;
+  std::sort(sorted.begin(), sorted.end());
+  const size_t n = sorted.size();
+  const double median = (n % 2) ? sorted[n / 2] : (sorted[n / 2 - 1] + sorted[n / 2]) / 2.0;
+  const double kmax = sorted.back();
+  const double rho = median > 0 ? kmax / median : INFINITY;
+  const bool on = rho >= (double)gate_tau;
+  *gate_on = on ? 1 : 0;
+  for (size_t i = 0; i < n; i++) {
+    double sv = 1.0;
+    if (on && ak[i] > 0 && aq[i] > 0) sv = std::pow(ak[i], (double)alpha) / std::pow(aq[i], 1.0 - (double)alpha);
+    const float s32 = (float)sv;
+    s[i] = s32;
+    inv_s[i] = (float)(1.0 / (double)s32);
+  }
+  return ok();
+}
+
+hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const void* k, const void* v,
+                                const float* s, const float* inv_s, void* q_codes, void* q_scales,
+                                void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                                void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  if ((s == nullptr) != (inv_s == nullptr)) return fail(HIFA4_ERR_NULL, "quantize: pass both s and inv_s or neither");
+  if (q && (!q_codes || !q_scales)) return fail(HIFA4_ERR_NULL, "quantize: q outputs are NULL");
+  if (k && (!k_codes || !k_scales)) return fail(HIFA4_ERR_NULL, "quantize: k outputs are NULL");
+  if (v && (!v_codes || !v_scales)) return fail(HIFA4_ERR_NULL, "quantize: v outputs are NULL");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const int group = dims->heads_q / dims->heads_kv;
+  if (q) {
+    hifa4::QuantRowsArgs a{(const uint16_t*)q, s, (int64_t)dims->batch * dims->heads_q * dims->len_q,
+                           dims->len_q, dims->heads_q, group, dims->head_dim, (uint8_t*)q_codes,
+                           (uint8_t*)q_scales};
+    hipError_t e = hifa4::launch_quantize_rows(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
+  }
+  if (k) {
+    hifa4::QuantRowsArgs a{(const uint16_t*)k, inv_s, (int64_t)dims->batch * dims->heads_kv * dims->len_kv,
+                           dims->len_kv, dims->heads_kv, 1, dims->head_dim, (uint8_t*)k_codes,
+                           (uint8_t*)k_scales};
+    hipError_t e = hifa4::launch_quantize_rows(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
+  }
+  if (v) {
+    hifa4::QuantVtArgs a{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
+                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales};
+    hipError_t e = hifa4::launch_quantize_vt(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize v: ") + hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts) {
+  if (check_dims(dims) != HIFA4_OK || check_opts(dims, opts) != HIFA4_OK) return 0;
+  return resolve_splits(dims, opts);
+}
+
+size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_opts* opts) {
+  if (check_dims(dims) != HIFA4_OK || check_opts(dims, opts) != HIFA4_OK) return 0;
+  if (dims->len_q != 1) return 0;
+  const int64_t parts = (int64_t)dims->batch * dims->heads_q * resolve_splits(dims, opts);
+  return align256((size_t)parts * dims->head_dim * 2) + align256((size_t)parts * 2 * 2);
+}
+
+hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* opts,
+                                 const void* q_codes, const void* q_scales, const void* k_codes,
+                                 const void* k_scales, const void* v_codes, const void* v_scales,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 float* tile_stats, void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  st = check_opts(dims, opts);
+  if (st != HIFA4_OK) return st;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+    return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
+  hifa4::AttnArgs a{};
+  a.q_codes = (const uint8_t*)q_codes;
+  a.q_scales = (const uint8_t*)q_scales;
+  a.k_codes = (const uint8_t*)k_codes;
+  a.k_scales = (const uint8_t*)k_scales;
+  a.v_codes = (const uint8_t*)v_codes;
+  a.v_scales = (const uint8_t*)v_scales;
+  a.out = (uint16_t*)out;
+  a.stats = tile_stats;
+  a.batch = dims->batch;
+  a.heads_q = dims->heads_q;
+  a.heads_kv = dims->heads_kv;
+  a.d = dims->head_dim;
+  a.len_q = dims->len_q;
+  a.len_kv = dims->len_kv;
+  a.len_kv32 = round32(dims->len_kv);
+  a.kv_tile = opts->kv_tile;
+  a.n_tiles = (int32_t)((dims->len_kv + opts->kv_tile - 1) / opts->kv_tile);
+  a.causal = opts->causal;
+  a.normalizer = opts->normalizer;
+  a.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+  exp2_cubic(&a.c1, &a.c2, &a.c3);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  hipError_t e;
+  if (dims->len_q == 1) {
+    if (tile_stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
+    const size_t need = hifa4_attention_workspace_bytes(dims, opts);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(HIFA4_ERR_WORKSPACE, "attention: decode needs " + std::to_string(need) + " workspace bytes");
+    a.num_splits = resolve_splits(dims, opts);
+    a.tiles_per_split = (a.n_tiles + a.num_splits - 1) / a.num_splits;
+    const int64_t parts = (int64_t)dims->batch * dims->heads_q * a.num_splits;
+    a.part_o = (uint16_t*)workspace;
+    a.part_ml = (uint16_t*)((char*)workspace + align256((size_t)parts * dims->head_dim * 2));
+    e = hifa4::launch_attn_decode(a, stream);
+  } else {
+    a.num_splits = 1;
+    a.tiles_per_split = a.n_tiles;
+    e = hifa4::launch_attn_prefill(a, stream);
+  }
+  if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

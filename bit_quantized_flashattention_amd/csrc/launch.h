@@ -1,0 +1,59 @@
+// Internal launch interface between the C ABI (hifa4_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hifa4 {
+
+struct QuantRowsArgs {
+  const uint16_t* x;    // FP16 [rows, d]
+  const float* scale;   // FP32 [Hs, d] or nullptr
+  int64_t rows;         // B * H * L
+  int64_t len;          // L
+  int32_t heads;        // H
+  int32_t heads_per_scale_row;  // query heads per KV head for Q (Hq/Hkv), 1 for K
+  int32_t d;
+  uint8_t* codes;       // [rows, d/2]
+  uint8_t* scales;      // [rows, d/32]
+};
+
+struct QuantVtArgs {
+  const uint16_t* v;    // FP16 [B*Hkv, L, d]
+  int64_t bh;           // B * Hkv
+  int64_t len;          // L
+  int64_t len32;        // L rounded up to 32
+  int32_t d;
+  uint8_t* codes;       // [B*Hkv, d, len32/2]
+  uint8_t* scales;      // [B*Hkv, d, len32/32]
+};
+
+struct AttnArgs {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  uint16_t* out;        // FP16 [B, Hq, Lq, d]
+  float* stats;         // FP32 [B, Hq, ceil(Lq/32), n_tiles, 2] or nullptr
+  uint16_t* part_o;     // decode: FP16 [B*Hq*S, d]
+  uint16_t* part_ml;    // decode: FP16 [B*Hq*S, 2] (m, l)
+  int32_t batch, heads_q, heads_kv, d;
+  int64_t len_q, len_kv, len_kv32;
+  int32_t kv_tile;      // keys per tile (64 or 128)
+  int32_t n_tiles;      // ceil(Lk / kv_tile)
+  int32_t causal;
+  int32_t normalizer;
+  int32_t num_splits;
+  int32_t tiles_per_split;
+  float c_log2;         // fp32(log2(e) / sqrt(d))
+  float c1, c2, c3;     // exp2 cubic coefficients
+};
+
+hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
+
+}  // namespace hifa4

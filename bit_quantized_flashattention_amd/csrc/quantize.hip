@@ -1,0 +1,140 @@
+// K1: Smooth-QK element-wise rescale + 4-bit block quantization (HBM-bound).
+//
+// HiFA4 abstract: Smooth-QK leaves only "a fusible element-wise scaling" at inference; here it is
+// fused into the quantizer, so Q and K are read once in FP16 and written once as 4-bit codes.
+#include "device_common.h"
+#include "launch.h"
+
+namespace hifa4 {
+
+// One thread per 32-element block along d: 64 B of FP16 in, 16 B of codes + 1 scale byte out.
+// Consecutive threads own consecutive blocks, so loads and stores are contiguous per wave.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
+  constexpr int NB = D / kBlock;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.rows * NB) return;
+  const int64_t row = t / NB;
+  const int blk = (int)(t % NB);
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + row * D + blk * kBlock);
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) raw[i] = src[i];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFF));
+      const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+      v[i * 8 + 2 * j] = (float)lo;
+      v[i * 8 + 2 * j + 1] = (float)hi;
+    }
+  }
+  if (a.scale != nullptr) {
+    const int h = (int)((row / a.len) % a.heads);
+    const float4* sc = reinterpret_cast<const float4*>(a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float4 s4 = sc[i];
+      v[4 * i + 0] = v[4 * i + 0] * s4.x;  // one FP32 rounding (contraction is off)
+      v[4 * i + 1] = v[4 * i + 1] * s4.y;
+      v[4 * i + 2] = v[4 * i + 2] * s4.z;
+      v[4 * i + 3] = v[4 * i + 3] * s4.w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+  const float sc = e8m0_as_float(e);
+  uint4 out;
+  out.x = pack8_fp4(v + 0, sc);
+  out.y = pack8_fp4(v + 8, sc);
+  out.z = pack8_fp4(v + 16, sc);
+  out.w = pack8_fp4(v + 24, sc);
+  *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + blk * 16) = out;
+  a.scales[row * NB + blk] = (uint8_t)(e + 127);
+}
+
+// V: blocks run along tokens, so a work-group stages 128 tokens x d channels in LDS and each
+// thread quantizes (channel, 32-token block) items, writing the transposed [d, L] layout.
+template <int D>
+constexpr int vt_tokens() { return D >= 256 ? 64 : 128; }  // LDS tile stays below 64 KB
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
+  constexpr int TOK = vt_tokens<D>();
+  constexpr int NBT = TOK / kBlock;  // 32-token blocks per tile
+  constexpr int ROW = D + 8;  // FP16 elements per LDS row (padding breaks bank aliasing)
+  __shared__ _Float16 tile[TOK * ROW];
+  const int64_t bh = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * TOK;
+  const uint16_t* src = a.v + bh * a.len * D;
+  constexpr int CPR = D / 8;  // 16-byte chunks per token row
+  for (int c = threadIdx.x; c < TOK * CPR; c += blockDim.x) {
+    const int r = c / CPR, cc = c % CPR;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (t0 + r < a.len) val = *reinterpret_cast<const uint4*>(src + (t0 + r) * D + cc * 8);
+    *reinterpret_cast<uint4*>(&tile[r * ROW + cc * 8]) = val;
+  }
+  __syncthreads();
+  const int64_t nblk = (a.len32 - t0) / kBlock < NBT ? (a.len32 - t0) / kBlock : NBT;
+  for (int w = threadIdx.x; w < D * NBT; w += blockDim.x) {
+    const int ch = w / NBT, jb = w % NBT;
+    if (jb >= nblk) continue;
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      v[i] = (float)tile[(jb * kBlock + i) * ROW + ch];
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const int e = mx_exponent(amax);
+    const float sc = e8m0_as_float(e);
+    uint4 out;
+    out.x = pack8_fp4(v + 0, sc);
+    out.y = pack8_fp4(v + 8, sc);
+    out.z = pack8_fp4(v + 16, sc);
+    out.w = pack8_fp4(v + 24, sc);
+    const int64_t crow = bh * D + ch;
+    *reinterpret_cast<uint4*>(a.codes + crow * (a.len32 / 2) + t0 / 2 + jb * 16) = out;
+    a.scales[crow * (a.len32 / kBlock) + t0 / kBlock + jb] = (uint8_t)(e + 127);
+  }
+}
+
+template <int D>
+static hipError_t quant_rows_d(const QuantRowsArgs& a, hipStream_t s) {
+  const int64_t items = a.rows * (D / kBlock);
+  const int64_t grid = (items + 255) / 256;
+  hipLaunchKernelGGL(quantize_rows_kernel<D>, dim3((uint32_t)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return quant_rows_d<64>(a, s);
+    case 128: return quant_rows_d<128>(a, s);
+    case 256: return quant_rows_d<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+static hipError_t quant_vt_d(const QuantVtArgs& a, hipStream_t s) {
+  const int64_t tiles = (a.len + vt_tokens<D>() - 1) / vt_tokens<D>();
+  hipLaunchKernelGGL(quantize_vt_kernel<D>, dim3((uint32_t)tiles, (uint32_t)a.bh), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return quant_vt_d<64>(a, s);
+    case 128: return quant_vt_d<128>(a, s);
+    case 256: return quant_vt_d<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hifa4

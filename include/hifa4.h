@@ -1,0 +1,146 @@
+/*
+ * hifa4.h -- C ABI of the MI355X (gfx950) 4-bit FlashAttention forward library (libhifa4.so).
+ *
+ * The operation follows "HiFA4: Training-Free 4-bit FlashAttention on Ascend HIF4 NPUs for LLM
+ * Inference" (arXiv 2607.04302v1), Abstract: Q and K get a calibration-static per-channel
+ * Smooth-QK rescale after RoPE, Q, K, V are quantized to a 4-bit block format, and a tiled
+ * attention kernel runs QK^T and PV as 4-bit matrix products while keeping the online-softmax
+ * state (running max m, normalizer l, rescaled output O) in FP16.  The normalizer is accumulated
+ * from the same quantized probabilities P-hat that enter the PV product (P-Reordering).
+ *
+ * 4-bit format (the pages name it HIF4 without a bit layout; this library substitutes): E2M1
+ * codes (sign, 2 exponent bits, 1 mantissa bit: 0, .5, 1, 1.5, 2, 3, 4, 6) with one
+ * power-of-two E8M0 scale byte (2^(byte-127)) per block of 32 elements; two codes per byte,
+ * the lower-index element in the low nibble.
+ *
+ * Memory layouts (all row-major, contiguous, no padding between rows):
+ *   q        FP16 [B, Hq,  Lq, d]            k, v      FP16 [B, Hkv, Lk, d]
+ *   q_codes  u8   [B, Hq,  Lq, d/2]          q_scales  u8   [B, Hq,  Lq, d/32]
+ *   k_codes  u8   [B, Hkv, Lk, d/2]          k_scales  u8   [B, Hkv, Lk, d/32]
+ *   v_codes  u8   [B, Hkv, d, Lk32/2]        v_scales  u8   [B, Hkv, d, Lk32/32]
+ *                 (V-hat is blocked along tokens; Lk32 = Lk rounded up to 32, tail tokens are 0)
+ *   out      FP16 [B, Hq,  Lq, d]
+ *   s, inv_s FP32 [Hkv, d]                   (query head h uses KV head h / (Hq/Hkv))
+ *
+ * Conventions: the caller owns every buffer; device pointers come from hipMalloc (or PyTorch's
+ * allocator); device calls are asynchronous on the given HIP stream (NULL = default stream) and
+ * never synchronize; no C++ exception crosses the ABI; a failed call launches nothing, returns a
+ * status and leaves a description in hifa4_last_error() (thread-local).  The only global state
+ * is that thread-local string, so calls from several threads are safe.
+ * Supported: d in {64, 128, 256}; Hq % Hkv == 0 and (Hq/Hkv <= 8 or Hq/Hkv % 8 == 0);
+ * Lq >= 1, Lk >= 1; causal requires Lq <= Lk (bottom-right aligned: key c is visible to query r
+ * iff c <= r + Lk - Lq).  Scores must satisfy |S * log2(e)/sqrt(d)| < 2048 (the running max is
+ * an FP16 integer).
+ */
+#ifndef HIFA4_H
+#define HIFA4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HIFA4_OK = 0,
+  HIFA4_ERR_NULL = 1,        /* a required pointer is NULL */
+  HIFA4_ERR_SHAPE = 2,       /* inconsistent or out-of-range dimensions */
+  HIFA4_ERR_UNSUPPORTED = 3, /* valid request this library does not implement */
+  HIFA4_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  HIFA4_ERR_HIP = 5          /* the HIP runtime reported an error (launch, device) */
+} hifa4_status;
+
+typedef struct {
+  int32_t batch;    /* B   >= 1 */
+  int32_t heads_q;  /* Hq  >= 1 */
+  int32_t heads_kv; /* Hkv >= 1, divides Hq */
+  int32_t head_dim; /* d in {64, 128, 256} */
+  int64_t len_q;    /* Lq  >= 1 */
+  int64_t len_kv;   /* Lk  >= 1 */
+} hifa4_dims;
+
+enum { HIFA4_P_REORDERED = 0, HIFA4_INCONSISTENT = 1 };
+
+typedef struct {
+  int32_t causal;     /* 0 or 1 */
+  int32_t normalizer; /* HIFA4_P_REORDERED: l from P-hat (the method); HIFA4_INCONSISTENT: l from
+                         the FP32 probabilities before quantization (the conventional formulation
+                         whose error Theorem 1 of the HiFA4 abstract describes) */
+  int32_t kv_tile;    /* keys per tile, 64 or 128; part of the numerical definition (the FP16
+                         state is rounded once per tile) */
+  int32_t num_splits; /* Lq == 1 only: split-KV count; 0 = choose automatically (see
+                         hifa4_decode_num_splits); part of the numerical definition */
+} hifa4_attn_opts;
+
+/*
+ * Smooth-QK calibration (host, synchronous).  [HiFA4 Abstract: the scale factors are computed
+ * once from a small offline calibration set.]  q_cal FP16 bits [Hq, N, d], k_cal FP16 bits
+ * [Hkv, N, d] (post-RoPE).  Per (KV head g, channel j): aK = max|k_cal[g, :, j]|, aQ = max over
+ * the tokens and the query heads of group g of |q_cal|.  Gate: rho = max(aK) / median(aK) over
+ * all (g, j); Smooth-QK is on iff rho >= gate_tau.  s = aK^alpha / aQ^(1-alpha) where on and both
+ * maxima are non-zero, else 1; outputs s (FP32 of s) and inv_s (FP32 of 1/s computed in FP64),
+ * both [Hkv, d] host arrays owned by the caller; *gate_on receives 0/1.
+ * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE (N < 1, Hq % Hkv != 0, d < 1, alpha outside [0, 1]).
+ */
+hifa4_status hifa4_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64_t n_tokens,
+                             int32_t heads_q, int32_t heads_kv, int32_t head_dim, float alpha,
+                             float gate_tau, float* s, float* inv_s, int32_t* gate_on);
+
+/*
+ * Smooth-QK rescale + 4-bit quantization (device, async).  [HiFA4 Abstract: only a fusible
+ * element-wise scaling remains at inference.]  Q' = fp32(Q * s[g(h)]), K' = fp32(K * inv_s[g]),
+ * V' = V; each 32-element block (Q, K along d; V along tokens) gets the exponent
+ * e = smallest with 6 * 2^e >= max|x| (clamped to [-127, 127], -127 for an all-zero block) and
+ * codes = round-to-nearest-even(x / 2^e) on the E2M1 grid (ties to the even code, sign copied).
+ * Any of q, k, v may be NULL to skip that tensor (its outputs are then not touched); s and inv_s
+ * may be NULL for no rescale (both or neither).  Outputs use the layouts above.
+ * Errors: HIFA4_ERR_NULL (an output of a present input is NULL), HIFA4_ERR_SHAPE,
+ * HIFA4_ERR_UNSUPPORTED (d), HIFA4_ERR_HIP.
+ */
+hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const void* k,
+                                const void* v, const float* s, const float* inv_s,
+                                void* q_codes, void* q_scales, void* k_codes, void* k_scales,
+                                void* v_codes, void* v_scales, void* hip_stream);
+
+/* Number of KV splits hifa4_attention_fwd uses for these dims and options (1 when Lq > 1). */
+int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts);
+
+/* Bytes of device workspace hifa4_attention_fwd needs (0 for prefill); 0 on invalid input. */
+size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_opts* opts);
+
+/*
+ * 4-bit attention forward (device, async).  [HiFA4 Abstract: QK^T and PV as 4-bit GEMMs,
+ * online-softmax state in FP16, P-Reordering fused into the PV product.]
+ * Per query row and per tile of kv_tile keys (ascending): S = Q-hat K-hat^T on the scaled FP4
+ * matrix cores; m_new = max(m, ceil(fp32(max S * C))) with C = fp32(log2(e)/sqrt(d));
+ * P-tilde = 2^floor(w) * g(fract(w)), w = fma(S, C, -m_new), g the cubic through the E2M1
+ * rounding midpoints; P-hat = E2M1 codes of P-tilde with one power-of-two scale per (query row,
+ * tile) ("each probability tile is quantized"), exponent by the rule above from the tile's
+ * largest score; PV and l-increment = rowsum(P-hat) from the same matrix-core pass;
+ * O = fp16(fma(2^(m_old-m_new), O, PV)), l likewise; out = fp16(O / l).
+ * Lq == 1 runs split-KV decode (num_splits partial FP16 states in the workspace, merged in
+ * split order); Lq > 1 runs the prefill kernel (workspace unused, may be NULL).
+ * tile_stats: NULL, or FP32 [B, Hq, ceil(Lq/32), ceil(Lk/kv_tile), 2] receiving, per block of 32
+ * query rows and key tile, (sum of P-hat, sum of P-tilde) over visible entries (zeros for tiles
+ * a row block never visits); prefill only.
+ * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE, HIFA4_ERR_UNSUPPORTED, HIFA4_ERR_WORKSPACE,
+ * HIFA4_ERR_HIP.
+ */
+hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* opts,
+                                 const void* q_codes, const void* q_scales, const void* k_codes,
+                                 const void* k_scales, const void* v_codes, const void* v_scales,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 float* tile_stats, void* hip_stream);
+
+/* Static description of a status code. */
+const char* hifa4_status_string(hifa4_status status);
+
+/* Detail of the last failure on the calling thread ("" if none); valid until the next call. */
+const char* hifa4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIFA4_H */

@@ -23,8 +23,13 @@ Readings where the pages are silent (each is listed in the design notes):
   ~1e-7 (relative) of a midpoint, and both sides take it in the same FP32
   arithmetic (the decision idea follows the FP4 attention prior art [FA4P],
   which maps scores straight to FP4 probabilities);
-* P-hat uses the same block format as Q, K, V: blocks of 32 keys per row; the
-  block exponent comes from X at the block's largest score;
+* P-hat ("each probability tile is quantized"): E2M1 codes with one power-of-two
+  scale per (query row, key tile), the exponent taken by the same no-clip rule
+  from X at the row's largest score in the tile.  A tile-level scale flushes
+  probabilities below ~1/16 of the tile maximum to zero, the net probability-
+  mass loss the abstract reports for every tile; it also keeps every sum of the
+  fused P-hat [V-hat | 1] product within 24 bits when V-hat's block scales are
+  close, so the matrix instruction's result is exact;
 * inside a scaled matrix instruction the four 32-element block products are
   each exact and are added to the accumulator in block order, with one FP32
   round-to-nearest-even per addition (``mfma_seq``);
@@ -248,19 +253,12 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
         mm = np.where(np.isfinite(m_new), m_new, F32(0)).astype(F32)
         w = fp.fma32(np.where(vt, st, F32(0)), c32, -mm[:, None])
         ptil = np.where(vt, exp2_x(w), F32(0)).astype(F32)
-        codes = np.zeros(st.shape, dtype=np.uint8)
-        eb = np.full((r_n, nb), -127, dtype=np.int64)
-        for j in range(nb):
-            sl = slice(32 * j, 32 * j + 32)
-            vb = vt[:, sl]
-            has = vb.any(axis=1)
-            bmax = np.where(vb, st[:, sl], F32(-np.inf)).max(axis=1)
-            bmax = np.where(has, bmax, F32(0)).astype(F32)
-            xb = exp2_x(fp.fma32(bmax, c32, -mm))
-            e = np.where(has, mx.scale_exponent(xb), -127)
-            eb[:, j] = e
-            y = ptil[:, sl].astype(F64) * np.exp2(-e.astype(F64))[:, None]
-            codes[:, sl] = np.where(vb, mx.rne_code(y), 0)
+        # P-hat: one power-of-two scale per (row, tile), from X at the tile's largest score
+        top = np.where(anyv, smax, F32(0)).astype(F32)
+        e_row = np.where(anyv, mx.scale_exponent(exp2_x(fp.fma32(top, c32, -mm))), -127)
+        y = ptil.astype(F64) * np.exp2(-e_row.astype(F64))[:, None]
+        codes = np.where(vt, mx.rne_code(y), 0).astype(np.uint8)
+        eb = np.repeat(e_row[:, None], nb, axis=1)
         ph = mx.code_half_units(codes)
         pv_blocks = []
         l_blocks = []
@@ -318,12 +316,9 @@ def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True
         mm = np.where(np.isfinite(m_new), m_new, 0.0)
         p = np.where(vt, np.exp2(np.where(vt, st, 0.0) * c64 - mm[:, None]), 0.0)
         if quantize:
-            ph = np.zeros_like(p)
-            for j in range(nb):
-                sl = slice(32 * j, 32 * j + 32)
-                e = mx.scale_exponent(p[:, sl].max(axis=1))
-                y = p[:, sl] * np.exp2(-e.astype(F64))[:, None]
-                ph[:, sl] = mx.code_value(mx.rne_code(y)) * np.exp2(e.astype(F64))[:, None]
+            e = mx.scale_exponent(p.max(axis=1))
+            y = p * np.exp2(-e.astype(F64))[:, None]
+            ph = mx.code_value(mx.rne_code(y)) * np.exp2(e.astype(F64))[:, None]
         else:
             ph = p
         pv = ph @ vvals[k0:k0 + bc]

@@ -18,6 +18,8 @@ Readings (the pages give no formula):
   inv32 = fp32(1 / s32) computed in FP64.
 """
 
+import math
+
 import numpy as np
 
 F32 = np.float32
@@ -45,8 +47,9 @@ def calibrate(q_cal, k_cal, alpha=0.5, tau=4.0):
     s = np.ones_like(a_k)
     if gate:
         ok = (a_k > 0) & (a_q > 0)
-        # array exponents: the C library pow for every element
-        s[ok] = np.power(a_k[ok], np.full(ok.sum(), alpha)) / np.power(a_q[ok], np.full(ok.sum(), 1.0 - alpha))
+        # the C library's pow, element by element
+        for idx in zip(*np.nonzero(ok)):
+            s[idx] = math.pow(a_k[idx], alpha) / math.pow(a_q[idx], 1.0 - alpha)
     s32 = s.astype(F32)
     inv32 = (1.0 / s32.astype(F64)).astype(F32)
     return s32, inv32, gate

@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/hifa4.h declares,
+rejects invalid arguments before launching anything, and calibrates like the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_flashattention_amd as hf
+from oracle import smooth
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hf.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hf.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hifa4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hifa4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.hifa4_status_string(0) == b"ok"
+    assert L.hifa4_status_string(5) == b"HIP runtime error"
+
+
+def test_attention_rejects_bad_arguments_without_launching(L):
+    dims = hf.make_dims(1, 4, 2, 128, 64, 64)
+    opts = hf.make_opts(causal=True)
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    args = [dummy] * 7
+    st = L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(opts), None, *args[:5], args[5], None, 0, None, None)
+    assert st == 1 and b"NULL" in L.hifa4_last_error()
+    bad = [hf.make_dims(1, 4, 3, 128, 64, 64), hf.make_dims(1, 4, 2, 96, 64, 64), hf.make_dims(0, 4, 2, 128, 64, 64),
+           hf.make_dims(1, 4, 2, 128, 65, 64), hf.make_dims(1, 24, 2, 128, 64, 64)]
+    want = [2, 3, 2, 2, 3]
+    for dm, w in zip(bad, want):
+        o = hf.make_opts(causal=True)
+        st = L.hifa4_attention_fwd(ctypes.byref(dm), ctypes.byref(o), *([dummy] * 7), None, 0, None, None)
+        assert st == w, (dm.heads_q, dm.heads_kv, dm.head_dim, dm.len_q, st, L.hifa4_last_error())
+    for o, w in [(hf.make_opts(kv_tile=96), 3), (hf.make_opts(normalizer=2), 2), (hf.Opts(2, 0, 128, 0), 2)]:
+        st = L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(o), *([dummy] * 7), None, 0, None, None)
+        assert st == w
+    # decode without workspace
+    dd = hf.make_dims(2, 8, 2, 128, 1, 4096)
+    o = hf.make_opts(causal=True)
+    assert L.hifa4_attention_workspace_bytes(ctypes.byref(dd), ctypes.byref(o)) > 0
+    st = L.hifa4_attention_fwd(ctypes.byref(dd), ctypes.byref(o), *([dummy] * 7), None, 0, None, None)
+    assert st == 4 and b"workspace" in L.hifa4_last_error()
+    assert L.hifa4_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(opts)) == 0
+
+
+def test_decode_splits_resolution(L):
+    d = hf.make_dims(64, 32, 8, 128, 1, 32768)
+    assert hf.decode_num_splits(d, hf.make_opts(causal=True, num_splits=0)) >= 1
+    assert hf.decode_num_splits(d, hf.make_opts(causal=True, num_splits=7)) == 7
+    small = hf.make_dims(1, 4, 1, 64, 1, 200)  # 2 tiles of 128: at most 2 splits
+    assert hf.decode_num_splits(small, hf.make_opts(num_splits=16)) == 2
+    assert hf.decode_num_splits(hf.make_dims(1, 4, 1, 64, 9, 200), hf.make_opts()) == 1
+
+
+def test_quantize_rejects_bad_arguments(L):
+    dims = hf.make_dims(1, 4, 2, 128, 64, 64)
+    dummy = ctypes.c_void_p(16)
+    st = L.hifa4_quantize_qkv(ctypes.byref(dims), dummy, None, None, dummy, None, None, None, None, None, None, None, None)
+    assert st == 1  # s without inv_s
+    st = L.hifa4_quantize_qkv(ctypes.byref(dims), dummy, None, None, None, None, None, None, None, None, None, None, None)
+    assert st == 1  # q present, outputs missing
+    bad = hf.make_dims(1, 4, 2, 80, 64, 64)
+    st = L.hifa4_quantize_qkv(ctypes.byref(bad), dummy, None, None, None, None, dummy, dummy, None, None, None, None, None)
+    assert st == 3
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 3])
+def test_calibrate_matches_oracle_bit_exactly(L, cfg_id):
+    cfg = synth.config(cfg_id)
+    qc, kc = synth.make_calibration(cfg)
+    s, inv, gate = hf.calibrate(qc, kc, cfg["alpha"], 4.0)
+    so, invo, gateo = smooth.calibrate(qc, kc, cfg["alpha"], 4.0)
+    assert gate == gateo and gate
+    assert np.array_equal(s.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(inv.view(np.uint32), invo.view(np.uint32))
+
+
+def test_calibrate_gate_off_and_errors(L):
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 32, 64)).astype(np.float16)
+    k = rng.standard_normal((2, 32, 64)).astype(np.float16)
+    s, inv, gate = hf.calibrate(q, k, 0.5, 4.0)
+    assert not gate and np.all(s == 1) and np.all(inv == 1)
+    with pytest.raises(hf.Hifa4Error):
+        hf.calibrate(q, k, 1.5, 4.0)
+    with pytest.raises(hf.Hifa4Error):
+        hf.calibrate(q[:3], k, 0.5, 4.0)

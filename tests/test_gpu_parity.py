@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, on seeded synthetic inputs.
+
+4-bit codes and scales must match bit for bit; attention outputs within max|d| <= 2e-3 * RMS of
+the oracle output.  Sizes span several tiles and ragged tails; edge cases cover GQA groups,
+d in {64, 128, 256}, both normalizers, both tile widths, causal with Lq < Lk and split-KV decode.
+"""
+import numpy as np
+import pytest
+
+import bit_quantized_flashattention_amd as hf
+from oracle import attention as A
+from oracle import mx
+import synth
+from gpu_helpers import compare_out, run_case, gpu_quantize, assert_codes_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def gen(cfg_id, **over):
+    cfg = synth.config(cfg_id, **over)
+    q, k, v = synth.make_qkv(cfg)
+    return cfg, q, k, v, synth.make_calibration(cfg)
+
+
+def test_library_loads_on_gpu():
+    import torch
+    assert torch.cuda.is_available()
+    hf.lib()
+
+
+def test_config0_full():
+    cfg, q, k, v, cal = gen(0)
+    print("case config0", flush=True)
+    got, want, qq, diag, _ = run_case(q, k, v, cfg["causal"], cfg["kv_tile"], calib=cal, alpha=cfg["alpha"])
+    compare_out(got, want, "config0")
+    assert diag.inexact_s == 0
+
+
+@pytest.mark.parametrize("normalizer", [A.P_REORDERED, A.INCONSISTENT])
+def test_qwen_shaped_reduced(normalizer):
+    cfg, q, k, v, cal = gen(1, B=1, Hq=8, Hkv=2, Lq=384, Lk=384)
+    print("case qwen-reduced norm", normalizer, flush=True)
+    got, want, qq, diag, _ = run_case(q, k, v, True, 128, normalizer, calib=cal)
+    compare_out(got, want, "qwen-reduced")
+
+
+@pytest.mark.parametrize("kv_tile", [64, 128])
+def test_ragged_noncausal_no_gqa(kv_tile):
+    cfg, q, k, v, cal = gen(1, B=2, Hq=2, Hkv=2, Lq=100, Lk=300)
+    print("case ragged kv_tile", kv_tile, flush=True)
+    got, want, *_ = run_case(q, k, v, False, kv_tile, calib=cal)
+    compare_out(got, want, "ragged-%d" % kv_tile)
+
+
+def test_causal_bottom_right_d64():
+    cfg, q, k, v, cal = gen(0, B=1, Hq=4, Hkv=2, Lq=77, Lk=333)
+    print("case causal-br d64", flush=True)
+    got, want, *_ = run_case(q, k, v, True, 64, calib=cal)
+    compare_out(got, want, "causal-br-d64")
+
+
+@pytest.mark.parametrize("normalizer", [A.P_REORDERED, A.INCONSISTENT])
+def test_gemma_shaped_d256(normalizer):
+    cfg, q, k, v, cal = gen(3, B=1, Hq=4, Hkv=2, Lq=300, Lk=300)
+    print("case gemma-d256 norm", normalizer, flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, normalizer, alpha=0.25, calib=cal)
+    compare_out(got, want, "gemma-d256")
+
+
+def test_wide_gqa_group_of_16():
+    cfg, q, k, v, cal = gen(1, B=1, Hq=32, Hkv=2, Lq=64, Lk=200)
+    print("case gqa16", flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, calib=cal)
+    compare_out(got, want, "gqa16")
+
+
+def test_v_all_ones_is_exactly_one():
+    cfg, q, k, v, cal = gen(1, B=1, Hq=8, Hkv=2, Lq=256, Lk=256)
+    v = np.ones_like(v)
+    print("case v-ones", flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, calib=cal)
+    assert np.all(got == 1.0) and np.all(want == 1.0)
+
+
+@pytest.mark.parametrize("d,splits,normalizer", [(128, 1, 0), (128, 3, 0), (128, 0, 0), (128, 0, 1), (64, 2, 0),
+                                                 (256, 4, 0)])
+def test_decode_split_kv(d, splits, normalizer):
+    cfg_id = 3 if d == 256 else 1
+    over = dict(B=3, Hq=8, Hkv=2, Lq=1, Lk=1000, d=d)
+    cfg, q, k, v, cal = gen(cfg_id, **over)
+    print("case decode d", d, "splits", splits, "norm", normalizer, flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, normalizer, calib=cal, num_splits=splits)
+    compare_out(got, want, "decode-d%d-s%d" % (d, splits))
+
+
+def test_tile_stats_match_oracle():
+    cfg, q, k, v, cal = gen(1, B=1, Hq=4, Hkv=1, Lq=200, Lk=200)
+    print("case stats", flush=True)
+    got, want, qq, diag, st = run_case(q, k, v, True, 64, calib=cal, stats=True)
+    compare_out(got, want, "stats-out")
+    for h in range(4):
+        for rb, t, sph, sp in A.tile_stats_p(qq, True, 64, 0, h):
+            assert np.isclose(st[0, h, rb, t, 0], sph, rtol=1e-5), (h, rb, t)
+            assert np.isclose(st[0, h, rb, t, 1], sp, rtol=1e-5), (h, rb, t)
+    # tiles above the causal diagonal of a row block are zero
+    assert st[0, 0, 0, 3, 0] == 0 and st[0, 0, 0, 3, 1] == 0
+
+
+def test_deterministic():
+    import torch
+    cfg, q, k, v, cal = gen(1, B=1, Hq=8, Hkv=2, Lq=300, Lk=300)
+    res = gpu_quantize(q, k, v, None, None)
+    dims = hf.make_dims(1, 8, 2, 128, 300, 300)
+    a = hf.attention_fwd(res, dims, True, 0, 128).clone()
+    b = hf.attention_fwd(res, dims, True, 0, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_quantizer_edge_values():
+    """Zero blocks, signed zeros, tiny and huge FP16 values, ragged V tail: codes bit-exact."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 2, 40, 64)).astype(np.float16)
+    k = rng.standard_normal((1, 1, 70, 64)).astype(np.float16)
+    v = rng.standard_normal((1, 1, 70, 64)).astype(np.float16)
+    q[0, 0, 0] = 0
+    q[0, 0, 1] = -0.0
+    q[0, 0, 2, :32] = np.float16(6e-8)
+    q[0, 0, 3, :32] = np.float16(65504)
+    q[0, 0, 3, 5] = -np.float16(1e-7)
+    k[0, 0, 5] = np.float16(-0.0)
+    v[0, 0, 60:] = 0
+    v[0, 0, 3, :] = np.float16(-65504)
+    res = gpu_quantize(q, k, v, None, None)
+    assert_codes_equal(res, A.quantize_qkv(q, k, v))
+    s = np.full((1, 64), 3.0, np.float32)
+    inv = (1.0 / s.astype(np.float64)).astype(np.float32)
+    res = gpu_quantize(q, k, v, s, inv)
+    assert_codes_equal(res, A.quantize_qkv(q, k, v, s, inv))

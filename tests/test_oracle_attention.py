@@ -197,18 +197,11 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
             m_new = max(m, tm)
             alpha = 0.0 if m == -math.inf else 2.0 ** (m - m_new)
             ptil = {cc: float(A.exp2_x(fp.fma32(svals[cc], c, F32(-m_new)))) for cc in keys}
-            phat = {}
-            escale = {}
-            for blk0 in range(t * bc, t * bc + bc, 32):
-                ks = [cc for cc in keys if blk0 <= cc < blk0 + 32]
-                if not ks:
-                    escale[blk0] = -127
-                    continue
-                top = max(svals[cc] for cc in ks)
-                e = int(mx.scale_exponent(np.array([float(A.exp2_x(fp.fma32(top, c, F32(-m_new))))]))[0])
-                escale[blk0] = e
-                for cc in ks:
-                    phat[cc] = int(mx.code_half_units(mx.rne_code(np.array([ptil[cc] * 2.0 ** -e])))[0])
+            # one P-hat scale for the row in this tile, from the tile's largest score
+            top = max(svals.values())
+            e = int(mx.scale_exponent(np.array([float(A.exp2_x(fp.fma32(top, c, F32(-m_new))))]))[0])
+            escale = {blk0: e for blk0 in range(t * bc, t * bc + bc, 32)}
+            phat = {cc: int(mx.code_half_units(mx.rne_code(np.array([ptil[cc] * 2.0 ** -e])))[0]) for cc in keys}
             pv = np.zeros(d, dtype=F32)
             for ch in range(d):
                 acc = 0.0
