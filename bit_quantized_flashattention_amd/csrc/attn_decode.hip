@@ -173,8 +173,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
     uint2 w;
-    w.x = (uint32_t)__builtin_bit_cast(uint16_t, o[cb][0][0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[cb][0][1]) << 16);
-    w.y = (uint32_t)__builtin_bit_cast(uint16_t, o[cb][1][0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[cb][1][1]) << 16);
+    w.x = __builtin_bit_cast(uint32_t, o[cb][0]);  // element 0 in the low half
+    w.y = __builtin_bit_cast(uint32_t, o[cb][1]);
     *reinterpret_cast<uint2*>(po + 16 * cb + 4 * g) = w;
   }
   if (g == 0) {
