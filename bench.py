@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the 4-bit (HiFA4-style) attention forward on one MI355X.
+
+A step is one pass of the hot path over one batch of resident synthetic input:
+the Smooth-QK rescale + 4-bit quantization of Q, K, V (HBM-bound kernel) followed
+by the fused 4-bit attention forward.  The default workload is the batched causal
+prefill (B=8, L=4096, Hq=32/Hkv=8, d=128, P-Reordered normalizer, 128-key tiles).
+The JSON line also carries the memory-bound split-KV decode (B=64, Lk=32768,
+pre-quantized cache; a step quantizes the query token and runs split + merge).
+
+    python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+
+Rates: algorithmic FLOPs are 4 * d per visible (query, key) pair (L(L+1)/2 pairs
+per head when causal); decode bytes are the K-hat/V-hat codes and scales, Q-hat
+and the FP16 output.  Kernel durations come from HIP events recorded on the
+stream the kernels run on.  Peaks: MI355X dense FP4 MFMA 10.1 PFLOP/s, HBM3E
+8 TB/s (AMD's published figures).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP4_PEAK_TFLOPS = 10100.0
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill-d256", "prefill-L2048"])
+    return p.parse_args()
+
+
+def causal_pairs(lq, lk):
+    shift = lk - lq
+    return sum(min(lk, r + shift + 1) for r in range(lq))
+
+
+def bench_prefill(args, cfg_id):
+    import torch
+    import bit_quantized_flashattention_amd as hf
+    import synth
+
+    cfg = synth.config(cfg_id)
+    b, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    q, k, v = synth.make_qkv_device(cfg)
+    q_cal, k_cal = synth.make_calibration(cfg)
+    s, inv, gate = hf.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
+    sd = torch.from_numpy(s).cuda()
+    invd = torch.from_numpy(inv).cuda()
+    dims = hf.make_dims(b, hq, hkv, d, lq, lk)
+    qkv = hf.quantize_qkv(q, k, v, sd, invd, dims=dims)
+    out = torch.empty((b, hq, lq, d), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        hf.quantize_qkv(q, k, v, sd, invd, dims=dims, out=qkv)
+        if ev is not None:
+            ev[0].record(stream)
+        hf.attention_fwd(qkv, dims, cfg["causal"], hf.P_REORDERED, cfg["kv_tile"], out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms = sum(a.elapsed_time(c) for a, c in evs) / args.steps
+    step_ms = (t1 - t0) * 1e3 / args.steps
+    pairs = causal_pairs(lq, lk) if cfg["causal"] else lq * lk
+    flops = 4.0 * d * pairs * b * hq
+    return dict(cfg=cfg, step_ms=step_ms, attn_ms=attn_ms, flops=flops, gate=gate,
+                qkv_inputs=(q, k, v), qkv=qkv, out=out)
+
+
+def bench_decode(args):
+    import torch
+    import bit_quantized_flashattention_amd as hf
+    import synth
+
+    cfg = synth.config(4)
+    b, hq, hkv, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lk"], cfg["d"]
+    q, k, v = synth.make_qkv_device(cfg)
+    q_cal, k_cal = synth.make_calibration(cfg)
+    s, inv, gate = hf.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
+    sd = torch.from_numpy(s).cuda()
+    invd = torch.from_numpy(inv).cuda()
+    dims = hf.make_dims(b, hq, hkv, d, 1, lk)
+    qkv = hf.quantize_qkv(q, k, v, sd, invd, dims=dims)  # the cache is quantized once
+    del k, v
+    torch.cuda.empty_cache()
+    opts = hf.make_opts(True, hf.P_REORDERED, cfg["kv_tile"], 0)
+    splits = hf.decode_num_splits(dims, opts)
+    ws = torch.empty(hf.attention_workspace_bytes(dims, opts), dtype=torch.uint8, device="cuda")
+    out = torch.empty((b, hq, 1, d), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        hf.quantize_qkv(q, None, None, sd, invd, dims=dims, out=qkv)
+        if ev is not None:
+            ev[0].record(stream)
+        hf.attention_fwd(qkv, dims, True, hf.P_REORDERED, cfg["kv_tile"], 0, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms = sum(a.elapsed_time(c) for a, c in evs) / n
+    step_ms = (t1 - t0) * 1e3 / n
+    lk32 = -(-lk // 32) * 32
+    kv_bytes = 2 * b * hkv * (lk * d // 2 + lk * d // 32)  # K-hat and V-hat codes + scales
+    assert kv_bytes == b * hkv * (lk * (d // 2 + d // 32) + d * (lk32 // 2 + lk32 // 32))
+    q_bytes = b * hq * (d // 2 + d // 32)
+    out_bytes = b * hq * d * 2
+    total = kv_bytes + q_bytes + out_bytes
+    res = {
+        "workload": "split-KV decode B%d Hq%d/Hkv%d d%d Lk%d, 4-bit cache, %d splits" % (b, hq, hkv, d, lk, splits),
+        "metric": "decode HBM GB/s",
+        "value": round(total / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "us_per_step": round(step_ms * 1e3, 1),
+        "bytes_per_step": total,
+        "roofline": {"bound": "hbm", "achieved": round(total / (attn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(total / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_us": round(attn_ms * 1e3, 1)},
+    }
+    del qkv, ws, out, q
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, pre):
+    """The oracle, as it stands, timed on host cores on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    from oracle import attention as A
+    from oracle import smooth
+
+    cfg = pre["cfg"]
+    q, k, v = pre["qkv_inputs"]
+    d, lq, lk, hq, hkv = cfg["d"], cfg["Lq"], cfg["Lk"], cfg["Hq"], cfg["Hkv"]
+    qh = q[0:1, 0:1].cpu().numpy()
+    kh = k[0:1, 0:1].cpu().numpy()
+    vh = v[0:1, 0:1].cpu().numpy()
+    import synth
+    q_cal, k_cal = synth.make_calibration(cfg)
+    s, inv, _ = smooth.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    qq = A.quantize_qkv(qh, kh, vh, s[:1], inv[:1])
+    flops = 0.0
+    rows_done = 0
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        rows = np.sort(rng.choice(lq, size=16, replace=False))
+        A.attention_head_p(qq, 0, 0, rows, cfg["causal"], cfg["kv_tile"], A.P_REORDERED)
+        shift = lk - lq
+        vis = np.minimum(lk, rows + shift + 1) if cfg["causal"] else np.full(len(rows), lk)
+        flops += 4.0 * d * float(vis.sum())
+        rows_done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "%d query rows of head (0,0) of the prefill workload incl. that head's quantization; %.1f s"
+                      % (rows_done, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (see DESIGN.md); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    cfg_id = {"prefill": 2, "prefill-d256": 3, "prefill-L2048": 1}[args.workload]
+    pre = bench_prefill(args, cfg_id)
+    cfg = pre["cfg"]
+    attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
+    step_tflops = pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "4-bit attention fwd TFLOP/s (+% FP4-MFMA peak); decode HBM GB/s",
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: causal=%s B%d Hq%d/Hkv%d d%d L%d, kv_tile %d, quantize + attention per step"
+                        % (cfg["name"], cfg["causal"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lq"],
+                           cfg["kv_tile"]),
+            "global_batch": cfg["B"], "seq_len": cfg["Lq"], "heads_q": cfg["Hq"], "heads_kv": cfg["Hkv"],
+            "head_dim": cfg["d"], "normalizer": "p_reordered", "smooth_qk_gate": pre["gate"],
+        },
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(pre["attn_ms"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, pre)
+    del pre
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = bench_decode(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,3 +127,42 @@ def make_calibration(cfg, seed_offset=0):
 def small(cfg_id, **override):
     """A reduced-size version of a config (same generator) for tests that the oracle finishes quickly."""
     return config(cfg_id, **override)
+
+
+def make_qkv_device(cfg, device="cuda", with_q=True, with_kv=True):
+    """Same distributions as make_qkv, drawn on the GPU with torch's seeded generator.
+
+    Used for the full-size workloads (the decode cache alone is 8.6 GB of FP16); the
+    values differ from make_qkv's (another random stream) but the recipe is identical.
+    Returns float16 CUDA tensors (None for parts not requested).
+    """
+    import torch
+    b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000 + cfg["id"])
+    gain = torch.tensor(_channel_gain(cfg, hkv, d), dtype=torch.float32, device=device)
+
+    def rope(x, positions):
+        if cfg["rope_theta"] is None:
+            return x
+        half = d // 2
+        i = torch.arange(half, device=device, dtype=torch.float64)
+        omega = cfg["rope_theta"] ** (-2.0 * i / d)
+        ang = (positions.to(torch.float64)[:, None] * omega[None, :])
+        c, s = torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
+        a, bb = x[..., :half], x[..., half:]
+        return torch.cat([a * c - bb * s, bb * c + a * s], dim=-1)
+
+    q = torch.empty((b_n, hq, lq, d), dtype=torch.float16, device=device) if with_q else None
+    k = torch.empty((b_n, hkv, lk, d), dtype=torch.float16, device=device) if with_kv else None
+    v = torch.empty((b_n, hkv, lk, d), dtype=torch.float16, device=device) if with_kv else None
+    qpos = torch.arange(lk - lq, lk, device=device)
+    kpos = torch.arange(lk, device=device)
+    for b in range(b_n):
+        if with_q:
+            q[b] = rope(torch.randn((hq, lq, d), generator=gen, device=device), qpos).to(torch.float16)
+        if with_kv:
+            kk = torch.randn((hkv, lk, d), generator=gen, device=device) * gain[:, None, :]
+            k[b] = rope(kk, kpos).to(torch.float16)
+            v[b] = torch.randn((hkv, lk, d), generator=gen, device=device).to(torch.float16)
+    return q, k, v
