@@ -111,8 +111,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
       s[k] = vis ? s[k] : -INFINITY;
       bmax = fmaxf(bmax, s[k]);
     }
-    float rmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float rmax = group_max4(bmax);
     const float m_new = fmaxf(m, __builtin_ceilf(rmax * C));
     float alpha = 1.0f;
     if (m_new != m) alpha = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
@@ -148,8 +147,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < 2; k++) t16[k] = t16[k] + t16[k + 2];
       const float sb = t16[0] + t16[1];
-      const float s01 = sb + __shfl_xor(sb, 16);
-      lsum = s01 + __shfl_xor(s01, 32);
+      lsum = group_sum4(sb);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {

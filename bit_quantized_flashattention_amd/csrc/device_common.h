@@ -69,4 +69,22 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, uint32_t sa, const uint4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950 row-swap
+// permutes, which are VALU operations (no LDS round trip).  Swapping a value with itself leaves
+// the lower partner's copy in the first result and the upper partner's in the second, in every
+// lane: v_permlane16_swap pairs rows (0,1) and (2,3), v_permlane32_swap pairs halves.
+__device__ __forceinline__ float group_max4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// (x0 + x1) + (x2 + x3) with x_g the value of lane group g, the same bits in every lane
+__device__ __forceinline__ float group_sum4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace hifa4
