@@ -16,29 +16,33 @@ Readings where the pages are silent (each is listed in the design notes):
 * scores are kept in the log2 domain: u = S * C with C = fp32(log2(e)/sqrt(d));
 * m is the running max of ceil(fp32(max_tile S * C)), an integer, so the
   rescale alpha = 2**(m_old - m_new) is exact and m is exact in FP16;
-* P-tilde = X(fma32(S, C, -m)) where X(w) = 2**floor(w) * g(fract(w)) and g is
-  the cubic with g(0) = 1 that passes through the three E2M1 rounding
-  midpoints 1.25, 1.5, 1.75 at log2 of those values.  The 4-bit decision on
-  P-tilde therefore equals round-to-nearest of the true 2**w except within
-  ~1e-7 (relative) of a midpoint, and both sides take it in the same FP32
-  arithmetic (the decision idea follows the FP4 attention prior art [FA4P],
-  which maps scores straight to FP4 probabilities);
+* the softmax runs on FP16 values, as the FP16 online-softmax state suggests:
+  P-tilde = 2**e * rn16(2**rn16(u)) with u = fma32(S, C, -(m + e)), i.e. the
+  log2-domain score, taken relative to the tile's scale 2**e, is rounded to
+  FP16 and exponentiated to a correctly rounded FP16 value;
 * P-hat ("each probability tile is quantized"): E2M1 codes with one power-of-two
-  scale per (query row, key tile), the exponent taken by the same no-clip rule
-  from X at the row's largest score in the tile.  A tile-level scale flushes
-  probabilities below ~1/16 of the tile maximum to zero, the net probability-
-  mass loss the abstract reports for every tile; it also keeps every sum of the
-  fused P-hat [V-hat | 1] product within 24 bits when V-hat's block scales are
+  scale 2**e per (query row, key tile); e is the smallest exponent that keeps
+  the row's largest probability in the tile inside the E2M1 range without
+  clipping, e = ceil(fp32(v - L6)) with v = fma32(max S, C, -m) and
+  L6 = fp32(log2 6), clamped to [-127, 127]; the codes are the round-to-
+  nearest-even E2M1 values of the FP16 probabilities rn16(2**rn16(u)) (the
+  decision idea follows the FP4 attention prior art [FA4P], which maps scores
+  straight to FP4 probabilities).  A tile-level scale flushes probabilities
+  below ~1/16 of the tile maximum to zero, the net probability-mass loss the
+  abstract reports for every tile; it also keeps every sum of the fused
+  P-hat [V-hat | 1] product within 24 bits when V-hat's block scales are
   close, so the matrix instruction's result is exact;
 * inside a scaled matrix instruction the four 32-element block products are
   each exact and are added to the accumulator in block order, with one FP32
   round-to-nearest-even per addition (``mfma_seq``);
-* O_new = fp16(fma32(alpha, O, PV)), l_new = fp16(fma32(alpha, l, L)) with PV
-  and L = rowsum(P-hat) from the same instruction sequence (ones column);
-  out = fp16(fp32(O) / fp32(l));
-* the inconsistent variant sums P-tilde in FP32 in a fixed tree order
-  (pairs (k, k+16), (k, k+8), ... inside each 32-key block, then
-  (s0 + s1) + (s2 + s3) over the blocks of a 128-key tile);
+* the state update is FP16 arithmetic: O_new = fma16(alpha, O, rn16(PV)),
+  l_new = fma16(alpha, l, rn16(L)) with alpha = rn16(2**(m_old - m_new)) and
+  PV, L = rowsum(P-hat) from the same instruction sequence (ones column), so
+  O and l follow one rule; out = fp16(fp32(O) / fp32(l));
+* the inconsistent variant sums the FP16 probabilities rn16(2**rn16(u)) in
+  FP32 in a fixed tree order (pairs (k, k+16), (k, k+8), ... inside each
+  32-key block, then (s0 + s1) + (s2 + s3) over the blocks of a 128-key
+  tile) and multiplies the sum by 2**e in FP32;
 * causal masking is bottom-right aligned: key c is visible to query r iff
   c <= r + (Lk - Lq);
 * split-KV decode: splits cover whole tiles, each split runs the recurrence
@@ -66,24 +70,27 @@ def softmax_scale_log2(d):
     return F32(math.log2(math.e) / math.sqrt(d))
 
 
-def _exp2_cubic():
-    """Coefficients of g(t) = 1 + c1 t + c2 t^2 + c3 t^3 with g(log2 v) = v for v in {1.25, 1.5, 1.75}."""
-    t = np.log2(np.array([1.25, 1.5, 1.75], dtype=F64))
-    a = np.stack([t, t * t, t * t * t], axis=1)
-    c = np.linalg.solve(a, np.array([0.25, 0.5, 0.75], dtype=F64))
-    return F32(c[0]), F32(c[1]), F32(c[2])
+LOG2_SIX = F32(math.log2(6.0))  # nearest FP32 to log2(6), pinned in the tests
 
 
-EXP2_C1, EXP2_C2, EXP2_C3 = _exp2_cubic()
+def tile_exponent(v):
+    """P-hat scale exponent of a (row, tile): e = ceil(fp32(v - L6)), clamped to [-127, 127].
+
+    v = fma32(max S, C, -m) is the log2 of the row's largest probability in the tile;
+    2**(v - e) then lies in (3, 6], inside the E2M1 range.
+    """
+    t = fp.add32(np.asarray(v, dtype=F32), -LOG2_SIX)
+    with np.errstate(invalid="ignore"):
+        e = np.ceil(t.astype(F64))
+    e = np.where(np.isfinite(e), e, -127.0)
+    return np.clip(e, -127, 127).astype(np.int64)
 
 
-def exp2_x(w):
-    """X(w) = ldexp(g(fract(w)), floor(w)) evaluated in FP32 (Horner, one rounding per fma)."""
-    w = np.asarray(w, dtype=F32)
-    n = fp.floor_i32(w)
-    f = fp.fract32(w)
-    g = fp.fma32(fp.fma32(fp.fma32(EXP2_C3, f, EXP2_C2), f, EXP2_C1), f, F32(1.0))
-    return fp.ldexp32(g, n)
+def exp2_16(u):
+    """FP16 probability rn16(2**rn16(u)) of FP32 log2-domain values u (correctly rounded twice)."""
+    h = fp.rn16(u)
+    with np.errstate(over="ignore"):
+        return fp.rn16(np.exp2(h.astype(F64)))
 
 
 def mfma_seq(blocks, acc=None):
@@ -250,14 +257,16 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
         with np.errstate(invalid="ignore", over="ignore"):
             alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2((m - m_new).astype(F64))))
         alpha = alpha.astype(F32)
+        alpha16 = fp.rn16(alpha)  # the state update runs in FP16
         mm = np.where(np.isfinite(m_new), m_new, F32(0)).astype(F32)
-        w = fp.fma32(np.where(vt, st, F32(0)), c32, -mm[:, None])
-        ptil = np.where(vt, exp2_x(w), F32(0)).astype(F32)
-        # P-hat: one power-of-two scale per (row, tile), from X at the tile's largest score
+        # P-hat: one power-of-two scale per (row, tile), from the tile's largest score
         top = np.where(anyv, smax, F32(0)).astype(F32)
-        e_row = np.where(anyv, mx.scale_exponent(exp2_x(fp.fma32(top, c32, -mm))), -127)
-        y = ptil.astype(F64) * np.exp2(-e_row.astype(F64))[:, None]
-        codes = np.where(vt, mx.rne_code(y), 0).astype(np.uint8)
+        e_row = np.where(anyv, tile_exponent(fp.fma32(top, c32, -mm)), -127)
+        big_m = (mm.astype(F64) + e_row).astype(F32)  # integers: exact
+        u = fp.fma32(np.where(vt, st, F32(0)), c32, -big_m[:, None])
+        p16 = np.where(vt, exp2_16(u), np.float16(0))
+        codes = np.where(vt, mx.rne_code(p16.astype(F64)), 0).astype(np.uint8)
+        ptil = p16.astype(F64) * np.exp2(e_row.astype(F64))[:, None]  # P-tilde, exact
         eb = np.repeat(e_row[:, None], nb, axis=1)
         ph = mx.code_half_units(codes)
         pv_blocks = []
@@ -273,11 +282,12 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
         pv, ok_pv = mfma_seq(pv_blocks)
         lsum, ok_l = mfma_seq(l_blocks)
         if mode == INCONSISTENT:
-            sums = [_tree_sum32(ptil[:, 32 * j:32 * j + 32]) for j in range(nb)]
+            sums = [_tree_sum32(p16[:, 32 * j:32 * j + 32].astype(F32)) for j in range(nb)]
             sums += [np.zeros(r_n, dtype=F32)] * (4 - nb) if nb < 4 else []
-            lsum = fp.add32(fp.add32(sums[0], sums[1]), fp.add32(sums[2], sums[3]))
-        o16 = fp.rn16(fp.fma32(alpha[:, None], o16.astype(F32), pv))
-        l16 = fp.rn16(fp.fma32(alpha, l16.astype(F32), lsum))
+            tree = fp.add32(fp.add32(sums[0], sums[1]), fp.add32(sums[2], sums[3]))
+            lsum = fp.mul32(tree, np.exp2(e_row.astype(F64)).astype(F32))
+        o16 = fp.fma16(alpha16[:, None], o16, fp.rn16(pv))
+        l16 = fp.fma16(alpha16, l16, fp.rn16(lsum))
         m = m_new
         if diag is not None:
             rows_touch = anyv
@@ -289,7 +299,7 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
                 for rb in np.unique(np.asarray(row_ids) // 32):
                     sel = (np.asarray(row_ids) // 32) == rb
                     if vt[sel].any():
-                        diag.stats.append((int(rb), t, float(phat[sel].sum()), float(ptil[sel].astype(F64).sum())))
+                        diag.stats.append((int(rb), t, float(phat[sel].sum()), float(ptil[sel].sum())))
     return State(m, l16, o16)
 
 

@@ -9,7 +9,8 @@ single, correct round-to-nearest-even step:
 * sums use an error-free two-sum in FP64 and fix the rare FP64 -> FP32 double
   rounding (when the FP64 sum lands exactly on an FP32 midpoint, the sign of
   the two-sum error decides the side);
-* FP16 rounding uses NumPy's correctly rounded float16 conversion.
+* FP16 rounding uses NumPy's correctly rounded float16 conversion; the FP16
+  fused multiply-add uses the same two-sum route with FP16 as the target.
 
 Every helper is pinned against ``fractions.Fraction`` brute force in
 ``tests/test_oracle_fp.py``.
@@ -24,24 +25,41 @@ F64 = np.float64
 ONE_MINUS_ULP32 = np.nextafter(F32(1.0), F32(0.0))
 
 
-def rn32_sum(a, b):
-    """Round the exact sum a + b (FP64 inputs) once to the nearest FP32 (ties to even)."""
+def _rn_sum(a, b, dtype):
+    """Round the exact sum a + b (FP64 inputs) once to ``dtype`` (float32 or float16), ties to even."""
     a = np.asarray(a, dtype=F64)
     b = np.asarray(b, dtype=F64)
     s = a + b
     bb = s - a
     err = (a - (s - bb)) + (b - bb)  # exact: a + b == s + err (two-sum)
     with np.errstate(over="ignore", invalid="ignore"):
-        r = s.astype(F32)
+        r = s.astype(dtype)
         r64 = r.astype(F64)
         diff = s - r64
-        toward = np.where(diff > 0, F32(np.inf), F32(-np.inf)).astype(F32)
+        toward = np.where(diff > 0, dtype(np.inf), dtype(-np.inf)).astype(dtype)
         o = np.nextafter(r, toward)
         o64 = o.astype(F64)
         at_mid = (diff != 0) & np.isfinite(s) & (np.abs(diff) == np.abs(o64 - s))
         # the true value s + err lies on the side of err; move to o when err points at o
         go_o = at_mid & (err != 0) & (np.sign(err) == np.sign(o64 - s))
-    return np.where(go_o, o, r).astype(F32)
+    return np.where(go_o, o, r).astype(dtype)
+
+
+def rn32_sum(a, b):
+    """Round the exact sum a + b (FP64 inputs) once to the nearest FP32 (ties to even)."""
+    return _rn_sum(a, b, F32)
+
+
+def fma16(a, b, c):
+    """FP16 fused multiply-add: RN16(a*b + c) with a single rounding (a, b, c are FP16 values).
+
+    The FP64 product of two FP16 values is exact (11 + 11 < 53 bits); the sum is rounded
+    once to FP16 through the two-sum route above.
+    """
+    a = np.asarray(a, dtype=np.float16).astype(F64)
+    b = np.asarray(b, dtype=np.float16).astype(F64)
+    c = np.asarray(c, dtype=np.float16).astype(F64)
+    return _rn_sum(a * b, c, np.float16)
 
 
 def fma32(a, b, c):

@@ -26,37 +26,87 @@ def rand_qkv(rng, b, hq, hkv, lq, lk, d, outlier=8.0):
     return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
 
 
-# ---------------------------------------------------------------- exp2 used for P-tilde
+# ---------------------------------------------------------------- FP16 probabilities and the tile scale
 
-def test_exp2_cubic_passes_through_midpoints():
-    g = lambda t: fp.fma32(fp.fma32(fp.fma32(A.EXP2_C3, t, A.EXP2_C2), t, A.EXP2_C1), t, F32(1))
-    for v in (1.25, 1.5, 1.75):
-        got = float(g(F32(math.log2(v))))
-        assert abs(got - v) <= 4 * 2.0 ** -23, (v, got)
-    n = np.arange(-149, 120)
-    assert np.array_equal(A.exp2_x(n.astype(F32)), np.ldexp(F32(1), n.astype(np.int32)).astype(F32))
+def _decimal_pow2(x, prec=50):
+    from decimal import Decimal, getcontext
+    getcontext().prec = prec
+    return Decimal(2) ** Decimal(float(x))
 
 
-def test_exp2_close_to_true_exp2_and_monotone():
-    w = np.linspace(-30, 3, 400001).astype(F32)
-    x = A.exp2_x(w).astype(np.float64)
-    rel = np.abs(x / np.exp2(w.astype(np.float64)) - 1)
-    assert rel.max() < 5e-4
-    inner = np.floor(w[1:]) == np.floor(w[:-1])
-    assert np.all(np.diff(x)[inner] >= -1e-7 * x[1:][inner])
+def test_exp2_16_is_correctly_rounded_for_every_fp16_input():
+    """rn16(2**h) through FP64 exp2 equals the correctly rounded value for all finite FP16 h.
+
+    The FP64 route is unambiguous when the FP64 result is farther than a few FP64 ulps from
+    every FP16 rounding midpoint; the test checks that margin for every input, and compares a
+    sample against 50-digit decimal arithmetic.
+    """
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    fin = np.isfinite(h)
+    h = h[fin]
+    y = np.exp2(h.astype(np.float64))
+    r = A.exp2_16(h.astype(F32))
+    assert np.array_equal(r, y.astype(np.float16))
+    # margin to the nearest FP16 midpoint (in the finite range)
+    ok = np.isfinite(r) & (r > 0)
+    lo = r[ok].astype(np.float64)
+    up = np.nextafter(r[ok], np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(r[ok], np.float16(0)).astype(np.float64)
+    mids = np.stack([(lo + up) / 2, (lo + dn) / 2], axis=1)
+    gap = np.min(np.abs(mids - y[ok][:, None]), axis=1)
+    assert np.all(gap > 8 * np.spacing(y[ok]))
+    # integer inputs are exact powers of two
+    ints = (h == np.round(h)) & (np.abs(h) <= 15)
+    assert np.array_equal(r[ints].astype(np.float64), np.exp2(h[ints].astype(np.float64)))
+    rng = np.random.default_rng(30)
+    from fractions import Fraction as Fr
+    from test_oracle_fp import rn_fraction_to_f16
+    for i in rng.choice(len(h), 400, replace=False):
+        if not (-25 < float(h[i]) < 15.9):
+            continue
+        want = rn_fraction_to_f16(Fr(str(_decimal_pow2(h[i]))))
+        assert r[i] == want, (h[i], r[i], want)
+
+
+def test_log2_six_is_the_nearest_fp32():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    ref = Decimal(6).ln() / Decimal(2).ln()
+    l6 = A.LOG2_SIX
+    lo = np.nextafter(l6, F32(0))
+    hi = np.nextafter(l6, F32(10))
+    d = abs(Decimal(float(l6)) - ref)
+    assert d < abs(Decimal(float(lo)) - ref) and d < abs(Decimal(float(hi)) - ref)
+
+
+def test_tile_exponent_is_the_no_clip_rule():
+    """e keeps the largest probability 2**v in (3, 6] * 2**e: the E2M1 no-clip rule of the block quantizer."""
+    v = -np.concatenate([np.linspace(0, 40, 400001), [0.0, 1.0, 2.5849, 2.585, 124.0, 125.0, 200.0]]).astype(F32)
+    e = A.tile_exponent(v)
+    want = mx.scale_exponent(np.exp2(v.astype(np.float64)))  # frexp-based rule on the exact value
+    # away from the boundaries v = log2(6) + k the two agree exactly
+    edge = np.abs((v.astype(np.float64) - math.log2(6)) - np.round(v.astype(np.float64) - math.log2(6))) < 1e-6
+    assert np.array_equal(e[~edge], want[~edge])
+    assert np.all(np.abs(e[edge] - want[edge]) <= 1)
+    top = np.exp2(v.astype(np.float64) - e)
+    inside = e > -127
+    assert np.all(top[inside] <= 6 * (1 + 1e-6)) and np.all(top[inside] > 3 * (1 - 1e-6))
+    assert A.tile_exponent(F32(0.0)) == -2 and A.tile_exponent(F32(-0.5)) == -3
+    assert A.tile_exponent(F32(-200.0)) == -127
 
 
 def test_p_codes_equal_rne_of_true_exp2_away_from_midpoints():
-    w = np.linspace(-4, 2.6, 2_000_001).astype(F32)
-    px = A.exp2_x(w).astype(np.float64)
-    pt = np.exp2(w.astype(np.float64))
-    for e in (-3, -2, -1, 0):
-        cx = mx.rne_code(px * 2.0 ** -e)
-        ct = mx.rne_code(pt * 2.0 ** -e)
-        mids = np.log2(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * 2.0 ** e)
-        near = np.min(np.abs(w.astype(np.float64)[:, None] - mids[None, :]), axis=1) < 1e-6
-        assert np.array_equal(cx[~near], ct[~near])
-        assert (cx[near] != ct[near]).sum() <= near.sum()
+    """E2M1 codes of the FP16 probabilities match those of the exact 2**u except near a midpoint."""
+    u = np.linspace(-4, 2.58, 2_000_001).astype(F32)
+    c16 = mx.rne_code(A.exp2_16(u).astype(np.float64))
+    ct = mx.rne_code(np.exp2(u.astype(np.float64)))
+    mids = np.log2(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]))
+    dist = np.min(np.abs(u.astype(np.float64)[:, None] - mids[None, :]), axis=1)
+    far = dist > 2.0 ** -8  # beyond FP16 rounding of u and of 2**u
+    assert np.array_equal(c16[far], ct[far])
+    assert np.all(np.abs(c16.astype(int) - ct.astype(int)) <= 1)
+    assert np.all(np.diff(c16.astype(int)) >= 0)  # monotone in u
 
 
 # ---------------------------------------------------------------- matrix-instruction model
@@ -166,7 +216,8 @@ def test_theorem1_coherent_scaling():
 
 def scalar_attention_p(qq, b, h, causal, bc, mode):
     """Level P by plain loops over rows, tiles, blocks and elements."""
-    from test_oracle_fp import rn_fraction_to_f32  # noqa: F401  (exactness helper is pinned there)
+    from fractions import Fraction as Fr
+    from test_oracle_fp import rn_fraction_to_f16
     hq, hkv = qq.qc.shape[1], qq.kc.shape[1]
     g = h // (hq // hkv)
     lq, d = qq.qc.shape[2], qq.qc.shape[3]
@@ -196,12 +247,18 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
             tm = math.ceil(float(F32(float(max(svals.values())) * float(c))))
             m_new = max(m, tm)
             alpha = 0.0 if m == -math.inf else 2.0 ** (m - m_new)
-            ptil = {cc: float(A.exp2_x(fp.fma32(svals[cc], c, F32(-m_new)))) for cc in keys}
-            # one P-hat scale for the row in this tile, from the tile's largest score
+            # one P-hat scale 2^e for the row in this tile, from the tile's largest score
             top = max(svals.values())
-            e = int(mx.scale_exponent(np.array([float(A.exp2_x(fp.fma32(top, c, F32(-m_new))))]))[0])
+            v_top = fp.fma32(top, c, F32(-m_new))
+            e = max(-127, math.ceil(float(F32(F32(v_top) - F32(math.log2(6.0))))))
+            big_m = F32(m_new + e)
+            p16 = {}
+            for cc in keys:
+                u = fp.fma32(svals[cc], c, -big_m)
+                p16[cc] = np.float16(math.pow(2.0, float(np.float16(u))))
+            ptil = {cc: float(p16[cc]) * 2.0 ** e for cc in keys}
             escale = {blk0: e for blk0 in range(t * bc, t * bc + bc, 32)}
-            phat = {cc: int(mx.code_half_units(mx.rne_code(np.array([ptil[cc] * 2.0 ** -e])))[0]) for cc in keys}
+            phat = {cc: int(mx.code_half_units(mx.rne_code(np.array([float(p16[cc])])))[0]) for cc in keys}
             pv = np.zeros(d, dtype=F32)
             for ch in range(d):
                 acc = 0.0
@@ -218,15 +275,18 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
             if mode == A.INCONSISTENT:
                 parts = []
                 for blk0 in range(t * bc, t * bc + 128, 32):
-                    vals = [F32(ptil.get(cc, 0.0)) for cc in range(blk0, blk0 + 32)]
+                    vals = [F32(p16.get(cc, 0.0)) for cc in range(blk0, blk0 + 32)]
                     while len(vals) > 1:
                         h2 = len(vals) // 2
                         vals = [F32(vals[j] + vals[j + h2]) for j in range(h2)]
                     parts.append(vals[0] if blk0 < t * bc + bc else F32(0))
-                lsum = F32(F32(parts[0] + parts[1]) + F32(parts[2] + parts[3]))
+                lsum = F32(F32(F32(parts[0] + parts[1]) + F32(parts[2] + parts[3])) * F32(2.0 ** e))
+            # FP16 state update: one rounding of alpha * O + fp16(PV), exact rationals
+            a16 = np.float16(alpha)
             for ch in range(d):
-                o16[ch] = np.float16(fp.fma32(F32(alpha), F32(o16[ch]), pv[ch]))
-            l16 = np.float16(fp.fma32(F32(alpha), F32(l16), lsum))
+                ex = Fr(float(a16)) * Fr(float(o16[ch])) + Fr(float(np.float16(pv[ch])))
+                o16[ch] = rn_fraction_to_f16(ex)
+            l16 = rn_fraction_to_f16(Fr(float(a16)) * Fr(float(l16)) + Fr(float(np.float16(lsum))))
             m = m_new
         out[r] = (o16.astype(F32) / F32(l16)).astype(np.float16)
     return out
