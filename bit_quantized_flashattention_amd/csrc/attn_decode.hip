@@ -87,7 +87,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   h2 o[CB][2];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) o[cb][0] = o[cb][1] = h2{(_Float16)0.0f, (_Float16)0.0f};
-  float l = 0.0f, m = -INFINITY;
+  _Float16 l = (_Float16)0.0f;
+  float m = -INFINITY;
 
   TileOps cur, nxt;
   if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
@@ -112,56 +113,25 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
       bmax = fmaxf(bmax, s[k]);
     }
     const float rmax = group_max4(bmax);
-    const float m_new = fmaxf(m, __builtin_ceilf(rmax * C));
-    float alpha = 1.0f;
-    if (m_new != m) alpha = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
-    const float negm = (m_new == -INFINITY) ? 0.0f : -m_new;
-    // P-hat: one scale per (query, tile) from the tile's largest score (all four lane groups agree)
-    int e = -127;
-    if (rmax != -INFINITY) e = mx_exponent(exp2_x(__builtin_fmaf(rmax, C, negm), a.c1, a.c2, a.c3));
-    const float scl = e8m0_as_float(e);
-    float p[32];
-#pragma unroll
-    for (int k = 0; k < 32; k++) {
-      const float x = exp2_x(__builtin_fmaf(s[k], C, negm), a.c1, a.c2, a.c3);
-      p[k] = s[k] == -INFINITY ? 0.0f : x;
-    }
-    uint4 ph;
-    ph.x = pack8_fp4(p + 0, scl);
-    ph.y = pack8_fp4(p + 8, scl);
-    ph.z = pack8_fp4(p + 16, scl);
-    ph.w = pack8_fp4(p + 24, scl);
-    const uint32_t psc = (uint32_t)(e + 127);
+    // integer running max, FP16 rescale factor and the P-hat scale of this tile (all four lane
+    // groups hold the same row maximum, so they agree)
+    const RowStep rs = row_step(rmax, m, C);
+    uint32_t p16[16];
+    const uint4 ph = phat_codes(s, C, rs.neg_big_m, p16);
+    const uint32_t psc = (uint32_t)(int)(rs.e + 127.0f);
     const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
     v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
     lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
     float lsum = lacc[0];
-    if (MODE == 1) {
-      float t16[16];
-#pragma unroll
-      for (int k = 0; k < 16; k++) t16[k] = p[k] + p[k + 16];
-#pragma unroll
-      for (int k = 0; k < 8; k++) t16[k] = t16[k] + t16[k + 8];
-#pragma unroll
-      for (int k = 0; k < 4; k++) t16[k] = t16[k] + t16[k + 4];
-#pragma unroll
-      for (int k = 0; k < 2; k++) t16[k] = t16[k] + t16[k + 2];
-      const float sb = t16[0] + t16[1];
-      lsum = group_sum4(sb);
-    }
+    if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16)) * e8m0_as_float((int)rs.e);
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
       v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
       pv = mfma_fp4(cur.v[cb], cur.vsc[cb], ph, psc, pv);
-#pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        const float o0 = __builtin_fmaf(alpha, (float)o[cb][hh][0], pv[2 * hh]);
-        const float o1 = __builtin_fmaf(alpha, (float)o[cb][hh][1], pv[2 * hh + 1]);
-        o[cb][hh] = h2{(_Float16)o0, (_Float16)o1};
-      }
+      state_update(o[cb], rs.alpha, pv);
     }
-    l = (float)(_Float16)__builtin_fmaf(alpha, l, lsum);
-    m = m_new;
+    l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
+    m = rs.m_new;
     if (tile + 1 < t_hi) cur = nxt;
   }
 

@@ -71,20 +71,6 @@ __device__ __forceinline__ float wave_sum16(float x) {  // sum over the 16 lanes
   return x;
 }
 
-// floor(x) as an int32 in one instruction (saturating; the argument is finite here)
-__device__ __forceinline__ int cvt_floor_i32(float x) {
-  int r;
-  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
-__device__ __forceinline__ float exp2_fast(float w, float c1, float c2, float c3) {
-  const float f = __builtin_amdgcn_fractf(w);
-  const int n = cvt_floor_i32(w);
-  const float g = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c3, f, c2), f, c1), f, 1.0f);
-  return __builtin_ldexpf(g, n);
-}
-
 template <int D>
 __device__ __forceinline__ void fetch_tile(Prefetch<D>& pf, const uint8_t* kc_g, const uint8_t* ks_g,
                                            const uint8_t* vc_g, const uint8_t* vs_g, int k0, int lk,
@@ -218,10 +204,11 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(AttnArgs a) {
 
   // ---- FP16 state; m is an integer-valued float
   h2 o[2][CB][2];
-  float l[2], m[2];
+  _Float16 l[2];
+  float m[2];
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
-    l[qb] = 0.0f;
+    l[qb] = (_Float16)0.0f;
     m[qb] = -INFINITY;
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) o[qb][cb][0] = o[qb][cb][1] = h2{(_Float16)0.0f, (_Float16)0.0f};
@@ -246,7 +233,6 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(AttnArgs a) {
   const uint8_t* vc_g = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / 2);
   const uint8_t* vs_g = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / kBlock);
   const float C = a.c_log2;
-  const float c1 = a.c1, c2 = a.c2, c3 = a.c3;
   const bool wave_live = q_base < lq;
   const int wave_last = q_base + 31 < lq - 1 ? q_base + 31 : lq - 1;
 
@@ -331,54 +317,22 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(AttnArgs a) {
           }
         }
         const float rmax = group_max4(bmax);
-        // ---- integer running max and the exact rescale factor
-        const float m_old = m[qb];
-        const float m_new = fmaxf(m_old, __builtin_ceilf(rmax * C));
-        float alpha = 1.0f;
-        if (m_new != m_old) alpha = (m_old == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m_old - m_new));
-        const float negm = (m_new == -INFINITY) ? 0.0f : -m_new;
-        // ---- P-hat: one scale per (query, tile) from the tile's largest score
-        int e = -127;
-        if (rmax != -INFINITY) e = mx_exponent(exp2_fast(__builtin_fmaf(rmax, C, negm), c1, c2, c3));
-        const float scl = e8m0_as_float(e);
-        float* p = s;  // P-tilde overwrites the scores in place
-        if (full) {
-#pragma unroll
-          for (int k = 0; k < 32; k++) p[k] = exp2_fast(__builtin_fmaf(s[k], C, negm), c1, c2, c3);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 32; k++) {
-            const bool vis = s[k] != -INFINITY;
-            const float x = exp2_fast(__builtin_fmaf(vis ? s[k] : 0.0f, C, negm), c1, c2, c3);
-            p[k] = vis ? x : 0.0f;
-          }
-        }
-        uint4 ph;
-        ph.x = pack8_fp4(p + 0, scl);
-        ph.y = pack8_fp4(p + 8, scl);
-        ph.z = pack8_fp4(p + 16, scl);
-        ph.w = pack8_fp4(p + 24, scl);
-        const uint32_t psc = (uint32_t)(e + 127);
+        // ---- integer running max, FP16 rescale factor, P-hat scale of this row and tile
+        const RowStep rs = row_step(rmax, m[qb], C);
+        uint32_t p16[16];
+        const uint4 ph = phat_codes(s, C, rs.neg_big_m, p16);
+        const uint32_t psc = (uint32_t)(int)(rs.e + 127.0f);
         // ---- normalizer increment: rowsum(P-hat) from the ones column, or the FP32 tree sum
         const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
         v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
         lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
         float lsum = lacc[0];
         if (MODE == 1 || STATS) {
-          float t16[16];
-#pragma unroll
-          for (int k = 0; k < 16; k++) t16[k] = p[k] + p[k + 16];
-#pragma unroll
-          for (int k = 0; k < 8; k++) t16[k] = t16[k] + t16[k + 8];
-#pragma unroll
-          for (int k = 0; k < 4; k++) t16[k] = t16[k] + t16[k + 4];
-#pragma unroll
-          for (int k = 0; k < 2; k++) t16[k] = t16[k] + t16[k + 2];
-          const float sb = t16[0] + t16[1];
-          const float ptree = group_sum4(sb);
+          const float sb = tree_sum32_h(p16);
+          const float ptree = group_sum4(sb) * e8m0_as_float((int)rs.e);
           if (MODE == 1) lsum = ptree;
           if (STATS) {
-            sum_p += sb;
+            sum_p += sb * e8m0_as_float((int)rs.e);
             sum_phat += (g == 0) ? lacc[0] : 0.0f;
           }
         }
@@ -387,15 +341,10 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(AttnArgs a) {
         for (int cb = 0; cb < CB; cb++) {
           v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
           pv = mfma_fp4(va[cb], vsc[cb], ph, psc, pv);
-#pragma unroll
-          for (int hh = 0; hh < 2; hh++) {
-            const float o0 = __builtin_fmaf(alpha, (float)o[qb][cb][hh][0], pv[2 * hh]);
-            const float o1 = __builtin_fmaf(alpha, (float)o[qb][cb][hh][1], pv[2 * hh + 1]);
-            o[qb][cb][hh] = h2{(_Float16)o0, (_Float16)o1};
-          }
+          state_update(o[qb][cb], rs.alpha, pv);
         }
-        l[qb] = (float)(_Float16)__builtin_fmaf(alpha, l[qb], lsum);
-        m[qb] = m_new;
+        l[qb] = __builtin_fmaf16(rs.alpha, l[qb], (_Float16)lsum);
+        m[qb] = rs.m_new;
       }
       if (STATS) {
         float sp = sum_p, sh = sum_phat;
@@ -421,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(AttnArgs a) {
   for (int qb = 0; qb < 2; qb++) {
     const int q = q_base + 16 * qb + col;
     if (q >= lq) continue;
-    const float lv = l[qb];
+    const float lv = (float)l[qb];
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
       const h2 r01 = h2{(_Float16)((float)o[qb][cb][0][0] / lv), (_Float16)((float)o[qb][cb][0][1] / lv)};

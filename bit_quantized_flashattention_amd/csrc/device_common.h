@@ -49,15 +49,118 @@ __device__ __forceinline__ uint32_t pack8_fp4(const float* v, float scale) {
   return w;
 }
 
-// P-tilde's exp2: X(w) = 2^floor(w) * g(fract(w)), g(t) = ((c3 t + c2) t + c1) t + 1 with one
-// rounding per fma.  g is the cubic through (0, 1) and the E2M1 rounding midpoints
-// (log2 1.25, 1.25), (log2 1.5, 1.5), (log2 1.75, 1.75), so a 4-bit decision on X(w) is the
-// round-to-nearest decision on the true 2^w except within ~1e-7 of a midpoint.
-__device__ __forceinline__ float exp2_x(float w, float c1, float c2, float c3) {
-  const float f = __builtin_amdgcn_fractf(w);
-  const float fl = __builtin_floorf(w);
-  const float g = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c3, f, c2), f, c1), f, 1.0f);
-  return __builtin_ldexpf(g, (int)fl);
+// log2(6) rounded to the nearest FP32 (0x40257007): 6 is the largest E2M1 magnitude.
+constexpr float kLog2Six = 0x1.4ae00ep+1f;
+
+// Exponent e of the P-hat scale 2^e of one (query row, key tile), as an integer-valued float:
+// the smallest power of two that keeps the row's largest probability 2^v in the tile inside the
+// E2M1 range, ceil(fp32(v - log2 6)), clamped below at -127 (v = -inf: no visible key).
+__device__ __forceinline__ float tile_exponent(float v) {
+  return fmaxf(__builtin_ceilf(v - kLog2Six), -127.0f);
+}
+
+// rn16(2^x) of both FP16 halves of h.  v_exp_f16 is correctly rounded on every FP16 input;
+// the SDWA form writes the high half and keeps the low one, so no pack is needed.  A
+// transcendental result is not forwarded to the next instruction: the SDWA form reads the low
+// half back (to keep it) only after one wait state, and so does the VALU consumer of r.
+__device__ __forceinline__ uint32_t exp2_h2(uint32_t h) {
+  uint32_t r;
+  asm("v_exp_f16 %0, %1\n\t"
+      "s_nop 0\n\t"
+      "v_exp_f16_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+      "s_nop 0"
+      : "=&v"(r)
+      : "v"(h));
+  return r;
+}
+
+// Packs the two FP16 values of p (scale 1) as E2M1 codes, RNE and saturating, into byte SEL
+// of old (the low half in the low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2_h(uint32_t old, uint32_t p) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(old, __builtin_bit_cast(h2, p), 1.0f, SEL);
+}
+
+// (FP16 a, FP16 b) in one dword, each rounded to nearest even
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
+
+// The FP32 value x as it is, kept from being folded into a mixed-precision instruction: the
+// log2-domain scores are rounded to FP32 by their fma first and only then to FP16.
+__device__ __forceinline__ float keep_f32(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// One (query row, key tile) step of the online softmax, from the row's largest visible score
+// rmax (-inf if none) and the running max m (-inf before the first visible key).
+struct RowStep {
+  float m_new;      // integer running max ceil(fp32(max S * C)), exact in FP16
+  _Float16 alpha;   // rn16(2^(m - m_new)), 0 while m = -inf: the FP16 rescale of O and l
+  float e;          // P-hat scale exponent of the row in this tile (integer-valued)
+  float neg_big_m;  // -(m_new + e): log2-domain offset of the scores relative to 2^e
+};
+
+__device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
+  RowStep r;
+  r.m_new = fmaxf(m, __builtin_ceilf(rmax * C));
+  const float al = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - r.m_new));
+  r.alpha = (_Float16)al;
+  const float mm = (r.m_new == -INFINITY) ? 0.0f : r.m_new;
+  r.e = tile_exponent(__builtin_fmaf(rmax, C, -mm));
+  r.neg_big_m = -(mm + r.e);
+  return r;
+}
+
+// P-hat codes of a lane's 32 keys: E2M1 of rn16(2^rn16(fma32(s_k, C, -(m + e)))), packed two
+// per byte, key 2j in the low nibble; a score of -inf (masked key) gives the code 0.  The FP16
+// probabilities are left in p16 (pairs) for callers that sum them.
+__device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, uint32_t* p16) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int k = 8 * q + 2 * j;
+      const float u0 = keep_f32(__builtin_fmaf(s[k], C, nbm));
+      const float u1 = keep_f32(__builtin_fmaf(s[k + 1], C, nbm));
+      const uint32_t pr = exp2_h2(pack_h2(u0, u1));
+      p16[k / 2] = pr;
+      if (j == 0) x = cvt_fp4x2_h<0>(x, pr);
+      if (j == 1) x = cvt_fp4x2_h<1>(x, pr);
+      if (j == 2) x = cvt_fp4x2_h<2>(x, pr);
+      if (j == 3) x = cvt_fp4x2_h<3>(x, pr);
+    }
+    w[q] = x;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// FP32 sum of the 32 FP16 probabilities of a lane in the fixed tree order: pairs (k, k + 16),
+// then (k, k + 8), (k, k + 4), (k, k + 2), (0, 1).
+__device__ __forceinline__ float tree_sum32_h(const uint32_t* p16) {
+  float t[32];
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const h2 v = __builtin_bit_cast(h2, p16[j]);
+    t[2 * j] = (float)v[0];
+    t[2 * j + 1] = (float)v[1];
+  }
+#pragma unroll
+  for (int w = 16; w >= 1; w /= 2) {
+#pragma unroll
+    for (int k = 0; k < w; k++) t[k] = t[k] + t[k + w];
+  }
+  return t[0];
+}
+
+// O <- fma16(alpha, O, rn16(pv)) for the four FP16 outputs of one accumulator tile.
+__device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& pv) {
+  const h2 a2 = h2{alpha, alpha};
+  o[0] = __builtin_elementwise_fma(a2, o[0], __builtin_bit_cast(h2, pack_h2(pv[0], pv[1])));
+  o[1] = __builtin_elementwise_fma(a2, o[1], __builtin_bit_cast(h2, pack_h2(pv[2], pv[3])));
 }
 
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, uint32_t sa, const uint4& b, uint32_t sb,

@@ -52,35 +52,6 @@ float half_bits_to_float(uint16_t h) {
   return f;
 }
 
-// Coefficients of the cubic g(t) = 1 + c1 t + c2 t^2 + c3 t^3 through the E2M1 rounding
-// midpoints (log2 v, v), v in {1.25, 1.5, 1.75}: Cramer's rule on the 3x3 Vandermonde-like system.
-void exp2_cubic(float* c1, float* c2, float* c3) {
-  const double t[3] = {std::log2(1.25), std::log2(1.5), std::log2(1.75)};
-  const double r[3] = {0.25, 0.5, 0.75};
-  double m[3][3];
-  for (int i = 0; i < 3; i++) {
-    m[i][0] = t[i];
-    m[i][1] = t[i] * t[i];
-    m[i][2] = t[i] * t[i] * t[i];
-  }
-  auto det3 = [](const double a[3][3]) {
-    return a[0][0] * (a[1][1] * a[2][2] - a[1][2] * a[2][1]) -
-           a[0][1] * (a[1][0] * a[2][2] - a[1][2] * a[2][0]) +
-           a[0][2] * (a[1][0] * a[2][1] - a[1][1] * a[2][0]);
-  };
-  const double det = det3(m);
-  double c[3];
-  for (int j = 0; j < 3; j++) {
-    double mj[3][3];
-    for (int i = 0; i < 3; i++)
-      for (int k = 0; k < 3; k++) mj[i][k] = (k == j) ? r[i] : m[i][k];
-    c[j] = det3(mj) / det;
-  }
-  *c1 = (float)c[0];
-  *c2 = (float)c[1];
-  *c3 = (float)c[2];
-}
-
 hifa4_status check_dims(const hifa4_dims* d) {
   if (d == nullptr) return fail(HIFA4_ERR_NULL, "dims is NULL");
   if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->len_q < 1 || d->len_kv < 1)
@@ -273,7 +244,6 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
   a.causal = opts->causal;
   a.normalizer = opts->normalizer;
   a.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
-  exp2_cubic(&a.c1, &a.c2, &a.c3);
   hipStream_t stream = (hipStream_t)hip_stream;
   hipError_t e;
   if (dims->len_q == 1) {

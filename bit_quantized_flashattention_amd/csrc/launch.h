@@ -48,7 +48,6 @@ struct AttnArgs {
   int32_t num_splits;
   int32_t tiles_per_split;
   float c_log2;         // fp32(log2(e) / sqrt(d))
-  float c1, c2, c3;     // exp2 cubic coefficients
 };
 
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);

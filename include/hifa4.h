@@ -114,11 +114,11 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * online-softmax state in FP16, P-Reordering fused into the PV product.]
  * Per query row and per tile of kv_tile keys (ascending): S = Q-hat K-hat^T on the scaled FP4
  * matrix cores; m_new = max(m, ceil(fp32(max S * C))) with C = fp32(log2(e)/sqrt(d));
- * P-tilde = 2^floor(w) * g(fract(w)), w = fma(S, C, -m_new), g the cubic through the E2M1
- * rounding midpoints; P-hat = E2M1 codes of P-tilde with one power-of-two scale per (query row,
- * tile) ("each probability tile is quantized"), exponent by the rule above from the tile's
- * largest score; PV and l-increment = rowsum(P-hat) from the same matrix-core pass;
- * O = fp16(fma(2^(m_old-m_new), O, PV)), l likewise; out = fp16(O / l).
+ * P-hat = E2M1 codes with one power-of-two scale 2^e per (query row, tile) ("each probability
+ * tile is quantized"), e = ceil(fp32(v - log2 6)) with v = fma(max S, C, -m_new), of the FP16
+ * probabilities rn16(2^rn16(fma(S, C, -(m_new + e)))) (P-tilde = 2^e times those); PV and the
+ * l-increment = rowsum(P-hat) from the same matrix-core pass; the state update is FP16
+ * arithmetic, O = fma16(rn16(2^(m_old - m_new)), O, rn16(PV)), l likewise; out = fp16(O / l).
  * Lq == 1 runs split-KV decode (num_splits partial FP16 states in the workspace, merged in
  * split order); Lq > 1 runs the prefill kernel (workspace unused, may be NULL).
  * tile_stats: NULL, or FP32 [B, Hq, ceil(Lq/32), ceil(Lk/kv_tile), 2] receiving, per block of 32
