@@ -163,8 +163,11 @@ def attention_workspace_bytes(dims, opts):
     return int(lib().hifa4_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(opts)))
 
 
+STATS_ROWS = 16  # query rows per tile-statistics block
+
+
 def stats_shape(dims, kv_tile):
-    return (dims.batch, dims.heads_q, -(-dims.len_q // 32), -(-dims.len_kv // kv_tile), 2)
+    return (dims.batch, dims.heads_q, -(-dims.len_q // STATS_ROWS), -(-dims.len_kv // kv_tile), 2)
 
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,

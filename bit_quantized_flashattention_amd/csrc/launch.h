@@ -36,7 +36,7 @@ struct AttnArgs {
   const uint8_t* v_codes;
   const uint8_t* v_scales;
   uint16_t* out;        // FP16 [B, Hq, Lq, d]
-  float* stats;         // FP32 [B, Hq, ceil(Lq/32), n_tiles, 2] or nullptr
+  float* stats;         // FP32 [B, Hq, ceil(Lq/16), n_tiles, 2] or nullptr
   uint16_t* part_o;     // decode: FP16 [B*Hq*S, d]
   uint16_t* part_ml;    // decode: FP16 [B*Hq*S, 2] (m, l)
   int32_t batch, heads_q, heads_kv, d;
@@ -47,6 +47,7 @@ struct AttnArgs {
   int32_t normalizer;
   int32_t num_splits;
   int32_t tiles_per_split;
+  int32_t heads_per_wg;  // prefill: query heads served by one work-group (set by the launcher)
   float c_log2;         // fp32(log2(e) / sqrt(d))
 };
 

@@ -121,7 +121,7 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * arithmetic, O = fma16(rn16(2^(m_old - m_new)), O, rn16(PV)), l likewise; out = fp16(O / l).
  * Lq == 1 runs split-KV decode (num_splits partial FP16 states in the workspace, merged in
  * split order); Lq > 1 runs the prefill kernel (workspace unused, may be NULL).
- * tile_stats: NULL, or FP32 [B, Hq, ceil(Lq/32), ceil(Lk/kv_tile), 2] receiving, per block of 32
+ * tile_stats: NULL, or FP32 [B, Hq, ceil(Lq/16), ceil(Lk/kv_tile), 2] receiving, per block of 16
  * query rows and key tile, (sum of P-hat, sum of P-tilde) over visible entries (zeros for tiles
  * a row block never visits); prefill only.
  * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE, HIFA4_ERR_UNSUPPORTED, HIFA4_ERR_WORKSPACE,

@@ -63,6 +63,7 @@ F32 = np.float32
 F64 = np.float64
 P_REORDERED = 0
 INCONSISTENT = 1
+STATS_ROWS = 16  # query rows per epsilon-statistics tile (a tile is 16 rows x kv_tile keys)
 
 
 def softmax_scale_log2(d):
@@ -296,8 +297,8 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
             diag.total_pv += int(rows_touch.sum()) * d
             if row_ids is not None:
                 phat = mx.code_value(codes) * np.exp2(np.repeat(eb, 32, axis=1).astype(F64))
-                for rb in np.unique(np.asarray(row_ids) // 32):
-                    sel = (np.asarray(row_ids) // 32) == rb
+                for rb in np.unique(np.asarray(row_ids) // STATS_ROWS):
+                    sel = (np.asarray(row_ids) // STATS_ROWS) == rb
                     if vt[sel].any():
                         diag.stats.append((int(rb), t, float(phat[sel].sum()), float(ptil[sel].sum())))
     return State(m, l16, o16)
@@ -421,7 +422,7 @@ def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None):
 
 
 def tile_stats_p(qq, causal, bc, b, h):
-    """Epsilon statistics of one head: list of (row_block_of_32, tile, sum P-hat, sum P-tilde)."""
+    """Epsilon statistics of one head: list of (row_block_of_16, tile, sum P-hat, sum P-tilde)."""
     diag = Diag()
     lq = qq.qc.shape[2]
     attention_head_p(qq, b, h, np.arange(lq), causal, bc, P_REORDERED, 1, diag, stats=True)
