@@ -39,8 +39,9 @@ __device__ __forceinline__ void load_tile(TileOps& t, const uint8_t* kc, const u
   for (int cb = 0; cb < D / 16; cb++) {
     const int ch = 16 * cb + col;
     const bool ok = 32 * g < bc && k0 + 32 * g < lk32;
-    t.v[cb] = ok ? *reinterpret_cast<const uint4*>(vc + (int64_t)ch * (lk32 / 2) + k0 / 2 + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-    t.vsc[cb] = ok ? vs[(int64_t)ch * (lk32 / kBlock) + k0 / kBlock + g] : 127u;
+    const int64_t cell = (k0 / kBlock + g) * D + ch;  // block-major V-hat: (32-key block, channel)
+    t.v[cb] = ok ? *reinterpret_cast<const uint4*>(vc + cell * 16) : make_uint4(0u, 0u, 0u, 0u);
+    t.vsc[cb] = ok ? vs[cell] : 127u;
   }
 }
 

@@ -49,15 +49,20 @@ struct Cfg {
   static constexpr int kScaleWords = kKScaleWords + D;
 };
 
+// Row stride in bytes of the V-hat scale rows in LDS: one row per 32-key block, padded so that the
+// four lane groups of a wave (one block each) read four different bank ranges.
+template <int D>
+constexpr int vs_stride() { return D + 16; }
+
 // One LDS buffer: K-hat codes [128 keys][D/2] (16-byte chunks XOR-swizzled, see kswz), K-hat
 // scales transposed [D/32 blocks][128 keys], V-hat^T codes [D][64] (chunks swizzled, see vswz),
-// V-hat scales [D][4].
+// V-hat scales [4 blocks][D] (rows vs_stride apart).
 template <int D>
 struct Tile {
   uint8_t kc[kTileKeys * (D / 2)];
   uint8_t ks[kTileKeys * (D / kBlock)];
   uint8_t vc[D * (kTileKeys / 2)];
-  uint8_t vs[D * (kTileKeys / kBlock)];
+  uint8_t vs[4 * vs_stride<D>()];
 };
 
 template <int D>
@@ -101,10 +106,10 @@ __device__ __forceinline__ void fetch_tile(Prefetch<D>& pf, const uint8_t* kc_g,
       const int r = c / CPR, part = c % CPR;
       if (r < bc && k0 + r < lk) w = *reinterpret_cast<const uint4*>(kc_g + (int64_t)(k0 + r) * (D / 2) + 16 * part);
     } else if (c < C::kChunks) {
-      const int cv = c - C::kKChunks;  // (channel, chunk) with 4 chunks of 16 bytes per channel
-      const int ch = cv >> 2, part = cv & 3;
+      const int cv = c - C::kKChunks;  // (32-key block, channel): 16 bytes, contiguous in HBM
+      const int part = cv / D, ch = cv % D;
       if (32 * part < bc && k0 + 32 * part < lk32)
-        w = *reinterpret_cast<const uint4*>(vc_g + (int64_t)ch * (lk32 / 2) + k0 / 2 + 16 * part);
+        w = *reinterpret_cast<const uint4*>(vc_g + ((int64_t)(k0 / kBlock + part) * D + ch) * 16);
     }
     pf.c[i] = w;
   }
@@ -121,19 +126,12 @@ __device__ __forceinline__ void fetch_tile(Prefetch<D>& pf, const uint8_t* kc_g,
       w = lo | (hi << 16);
     }
   } else if (tid < C::kScaleWords) {
-    const int ch = tid - C::kKScaleWords;
-    const uint8_t* src = vs_g + (int64_t)ch * (lk32 / kBlock) + k0 / kBlock;
-    const int nb = (lk32 - k0) / kBlock;  // V-hat blocks left in the row
-    if (bc == kTileKeys && nb >= 4 && (reinterpret_cast<uintptr_t>(src) & 3) == 0) {
-      w = *reinterpret_cast<const uint32_t*>(src);
-    } else {
-      uint32_t b0 = 0x7F, b1 = 0x7F, b2 = 0x7F, b3 = 0x7F;
-      if (nb > 0) b0 = src[0];
-      if (nb > 1 && bc > 32) b1 = src[1];
-      if (nb > 2 && bc > 64) b2 = src[2];
-      if (nb > 3 && bc > 96) b3 = src[3];
-      w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-    }
+    // V-hat scales of the tile: 4 blocks x D channels, contiguous in HBM; dword j holds channels
+    // 4j % D .. +3 of block 4j / D
+    const int j = tid - C::kKScaleWords;
+    const int part = 4 * j / D;
+    if (32 * part < bc && k0 + 32 * part < lk32)
+      w = *reinterpret_cast<const uint32_t*>(vs_g + (int64_t)(k0 / kBlock) * D + 4 * j);
   }
   pf.sw = w;
 }
@@ -152,7 +150,7 @@ __device__ __forceinline__ void store_tile(Tile<D>& t, const Prefetch<D>& pf, in
       *reinterpret_cast<uint4*>(&t.kc[r * (D / 2) + 16 * sw]) = pf.c[i];
     } else if (c < C::kChunks) {
       const int cv = c - C::kKChunks;
-      const int ch = cv >> 2, part = cv & 3;
+      const int part = cv / D, ch = cv % D;
       *reinterpret_cast<uint4*>(&t.vc[ch * 64 + 16 * vswz(ch, part)]) = pf.c[i];
     }
   }
@@ -165,7 +163,8 @@ __device__ __forceinline__ void store_tile(Tile<D>& t, const Prefetch<D>& pf, in
       t.ks[blk * kTileKeys + key] = (uint8_t)(pf.sw >> (8 * j));
     }
   } else if (tid < C::kScaleWords) {
-    *reinterpret_cast<uint32_t*>(&t.vs[(tid - C::kKScaleWords) * 4]) = pf.sw;
+    const int j = tid - C::kKScaleWords;
+    *reinterpret_cast<uint32_t*>(&t.vs[(4 * j / D) * vs_stride<D>() + (4 * j) % D]) = pf.sw;
   }
 }
 
@@ -241,13 +240,14 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
   const uint8_t* ks_g = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * (int64_t)lk * (D / kBlock);
   const uint8_t* vc_g = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / 2);
   const uint8_t* vs_g = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / kBlock);
+  // (both are the start of this (batch, KV head)'s block-major V-hat: lk32/32 blocks of D cells)
   const float C = a.c_log2;
 
   // per-lane LDS offsets of this lane's MFMA operands (see the loads in the tile loop)
   const int k_lane_off = (32 * (col >> 2) + (col & 3)) * (D / 2) + 16 * kswz<D>(32 * (col >> 2) + (col & 3), g);
   const int ks_lane_off = g * kTileKeys + 32 * (col >> 2) + (col & 3);
   const int v_lane_off = col * 64 + 16 * vswz(col, g);
-  const int vs_lane_off = col * 4 + g;
+  const int vs_lane_off = g * vs_stride<D>() + col;
 
   Prefetch<D> pf;
   fetch_tile<D>(pf, kc_g, ks_g, vc_g, vs_g, 0, lk, lk32, bc, tid);
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
         const uint4 va = *reinterpret_cast<const uint4*>(vbase + 16 * 64 * cb);
-        const uint32_t vsc = vsbase[16 * 4 * cb];
+        const uint32_t vsc = vsbase[16 * cb];
         v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
         pv = mfma_fp4(va, vsc, ph, psc, pv);
         state_update(o[cb], rs.alpha, pv);

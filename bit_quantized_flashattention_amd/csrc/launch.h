@@ -24,8 +24,8 @@ struct QuantVtArgs {
   int64_t len;          // L
   int64_t len32;        // L rounded up to 32
   int32_t d;
-  uint8_t* codes;       // [B*Hkv, d, len32/2]
-  uint8_t* scales;      // [B*Hkv, d, len32/32]
+  uint8_t* codes;       // [B*Hkv, len32/32, d, 16] (block-major)
+  uint8_t* scales;      // [B*Hkv, len32/32, d]
 };
 
 struct AttnArgs {

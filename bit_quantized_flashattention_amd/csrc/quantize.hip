@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
 }
 
 // V: blocks run along tokens, so a work-group stages 128 tokens x d channels in LDS and each
-// thread quantizes (channel, 32-token block) items, writing the transposed [d, L] layout.
+// thread quantizes (channel, 32-token block) items.  The output is block-major (for each
+// 32-token block, all channels), so consecutive threads write consecutive 16-byte cells.
 template <int D>
 constexpr int vt_tokens() { return D >= 256 ? 64 : 128; }  // LDS tile stays below 64 KB
 
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
   __syncthreads();
   const int64_t nblk = (a.len32 - t0) / kBlock < NBT ? (a.len32 - t0) / kBlock : NBT;
   for (int w = threadIdx.x; w < D * NBT; w += blockDim.x) {
-    const int ch = w / NBT, jb = w % NBT;
+    const int jb = w / D, ch = w % D;
     if (jb >= nblk) continue;
     float v[32];
     float amax = 0.0f;
@@ -98,9 +99,10 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
     out.y = pack8_fp4(v + 8, sc);
     out.z = pack8_fp4(v + 16, sc);
     out.w = pack8_fp4(v + 24, sc);
-    const int64_t crow = bh * D + ch;
-    *reinterpret_cast<uint4*>(a.codes + crow * (a.len32 / 2) + t0 / 2 + jb * 16) = out;
-    a.scales[crow * (a.len32 / kBlock) + t0 / kBlock + jb] = (uint8_t)(e + 127);
+    // block-major V-hat: [bh][token block][channel] -> 16 code bytes, one scale byte
+    const int64_t cell = (bh * (a.len32 / kBlock) + t0 / kBlock + jb) * D + ch;
+    *reinterpret_cast<uint4*>(a.codes + cell * 16) = out;
+    a.scales[cell] = (uint8_t)(e + 127);
   }
 }
 

@@ -17,8 +17,10 @@
  *   q        FP16 [B, Hq,  Lq, d]            k, v      FP16 [B, Hkv, Lk, d]
  *   q_codes  u8   [B, Hq,  Lq, d/2]          q_scales  u8   [B, Hq,  Lq, d/32]
  *   k_codes  u8   [B, Hkv, Lk, d/2]          k_scales  u8   [B, Hkv, Lk, d/32]
- *   v_codes  u8   [B, Hkv, d, Lk32/2]        v_scales  u8   [B, Hkv, d, Lk32/32]
- *                 (V-hat is blocked along tokens; Lk32 = Lk rounded up to 32, tail tokens are 0)
+ *   v_codes  u8   [B, Hkv, Lk32/32, d, 16]   v_scales  u8   [B, Hkv, Lk32/32, d]
+ *                 (V-hat is blocked along tokens and stored block-major: for each block of 32
+ *                 tokens, the 16 code bytes of channel 0, then channel 1, ...; a key tile is one
+ *                 contiguous run of bytes.  Lk32 = Lk rounded up to 32, tail tokens are 0)
  *   out      FP16 [B, Hq,  Lq, d]
  *   s, inv_s FP32 [Hkv, d]                   (query head h uses KV head h / (Hq/Hkv))
  *

@@ -134,9 +134,17 @@ class Quantized:
         self.lk = lk
 
     def packed(self):
-        """Bytes in the library's HBM layout: (q_codes, q_scales, k_codes, k_scales, v_codes, v_scales)."""
+        """Bytes in the library's HBM layout: (q_codes, q_scales, k_codes, k_scales, v_codes, v_scales).
+
+        Q-hat and K-hat are row-major as computed.  V-hat is stored token-block major: for each
+        32-token block, the 16 code bytes of every channel ([B, Hkv, Lk32/32, d, 16]) and the
+        scale bytes of every channel ([B, Hkv, Lk32/32, d]).
+        """
+        b, hkv, d, lk32 = self.vc.shape
+        vcode = mx.pack_codes(self.vc).reshape(b, hkv, d, lk32 // 32, 16).transpose(0, 1, 3, 2, 4)
+        vscale = np.swapaxes(mx.scale_bytes(self.ve), 2, 3)
         return (mx.pack_codes(self.qc), mx.scale_bytes(self.qe), mx.pack_codes(self.kc),
-                mx.scale_bytes(self.ke), mx.pack_codes(self.vc), mx.scale_bytes(self.ve))
+                mx.scale_bytes(self.ke), np.ascontiguousarray(vcode), np.ascontiguousarray(vscale))
 
 
 def quantize_qkv(q, k, v, s32=None, inv32=None):
