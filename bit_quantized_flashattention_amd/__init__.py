@@ -117,7 +117,7 @@ def quantized_shapes(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
     lk32 = -(-len_kv // 32) * 32
     return {
         "q_codes": (batch, heads_q, len_q, head_dim // 2), "q_scales": (batch, heads_q, len_q, head_dim // 32),
-        "k_codes": (batch, heads_kv, len_kv, head_dim // 2), "k_scales": (batch, heads_kv, len_kv, head_dim // 32),
+        "k_codes": (batch, heads_kv, len_kv, head_dim // 2), "k_scales": (batch, heads_kv, head_dim // 32, lk32),
         "v_codes": (batch, heads_kv, lk32 // 32, head_dim, 16), "v_scales": (batch, heads_kv, lk32 // 32, head_dim),
     }
 

@@ -12,36 +12,58 @@ namespace hifa4 {
 
 namespace {
 
+template <int D>
 struct TileOps {
-  uint4 k[8][2];      // K-hat A operands of the 8 score MFMAs (2 contraction steps for d = 256)
-  uint32_t ksc[8][2];
-  uint4 v[16];        // V-hat^T A operands of the 16-channel blocks (up to d = 256)
-  uint32_t vsc[16];
+  static constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
+  static constexpr int CB = D / 16;
+  uint4 k[8][KSTEPS];   // K-hat A operands of the 8 score MFMAs (2 contraction steps for d = 256)
+  uint2 ksc[KSTEPS];    // scale bytes of the 8 keys of the lane's MFMA row (byte t: MFMA t)
+  uint4 v[CB];          // V-hat^T A operands of the channel blocks
+  uint32_t vsc[CB / 4]; // scale bytes of the lane's CB channels (byte cb: block cb)
 };
 
+// HBM -> registers: this lane's MFMA operands of the tile at key k0 (see score_row_key and the
+// channel map in device_common.h); keys past lk (or past the tile) read as code 0.
 template <int D>
-__device__ __forceinline__ void load_tile(TileOps& t, const uint8_t* kc, const uint8_t* ks,
+__device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, const uint8_t* ks,
                                           const uint8_t* vc, const uint8_t* vs, int64_t k0,
                                           int64_t lk, int64_t lk32, int bc, int col, int g) {
-  constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
+  constexpr int KSTEPS = TileOps<D>::KSTEPS;
+  constexpr int CB = TileOps<D>::CB;
+  const bool lane_k = D >= 128 || g < 2;
 #pragma unroll
   for (int tt = 0; tt < 8; tt++) {
-    const int kr = 32 * (col >> 2) + 4 * tt + (col & 3);
+    const int kr = score_row_key(tt, col);
     const int64_t key = k0 + kr;
-    const bool ok = kr < bc && key < lk && (D >= 128 || g < 2);
+    const bool ok = kr < bc && key < lk && lane_k;
 #pragma unroll
-    for (int st = 0; st < KSTEPS; st++) {
+    for (int st = 0; st < KSTEPS; st++)
       t.k[tt][st] = ok ? *reinterpret_cast<const uint4*>(kc + key * (D / 2) + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-      t.ksc[tt][st] = ok ? ks[key * (D / kBlock) + 4 * st + g] : 127u;
-    }
   }
+  // the 8 keys k0 + 32 (col/4) + 8 (col%4) + 0..7 lie in one 32-key block of the padded rows
+  const int64_t kfirst = k0 + 32 * (col >> 2) + 8 * (col & 3);
 #pragma unroll
-  for (int cb = 0; cb < D / 16; cb++) {
-    const int ch = 16 * cb + col;
-    const bool ok = 32 * g < bc && k0 + 32 * g < lk32;
-    const int64_t cell = (k0 / kBlock + g) * D + ch;  // block-major V-hat: (32-key block, channel)
-    t.v[cb] = ok ? *reinterpret_cast<const uint4*>(vc + cell * 16) : make_uint4(0u, 0u, 0u, 0u);
-    t.vsc[cb] = ok ? vs[cell] : 127u;
+  for (int st = 0; st < KSTEPS; st++)
+    t.ksc[st] = (kfirst < lk32 && lane_k) ? *reinterpret_cast<const uint2*>(ks + (int64_t)(4 * st + g) * lk32 + kfirst)
+                                          : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const bool okv = 32 * g < bc && k0 + 32 * g < lk32;
+  const int64_t row = (k0 / kBlock + g) * D;  // block-major V-hat: cells (32-key block, channel)
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+    t.v[cb] = okv ? *reinterpret_cast<const uint4*>(vc + (row + CB * col + cb) * 16) : make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (CB == 4) {
+    t.vsc[0] = okv ? *reinterpret_cast<const uint32_t*>(vs + row + CB * col) : 0x7F7F7F7Fu;
+  } else if constexpr (CB == 8) {
+    const uint2 w = okv ? *reinterpret_cast<const uint2*>(vs + row + CB * col) : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    t.vsc[0] = w.x;
+    t.vsc[1] = w.y;
+  } else {
+    const uint4 w = okv ? *reinterpret_cast<const uint4*>(vs + row + CB * col)
+                        : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    t.vsc[0] = w.x;
+    t.vsc[1] = w.y;
+    t.vsc[2] = w.z;
+    t.vsc[3] = w.w;
   }
 }
 
@@ -79,7 +101,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   }
 
   const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);
-  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk * (D / kBlock);
+  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk32 * (D / kBlock);
   const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / 2);
   const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / kBlock);
   const float C = a.c_log2;
@@ -91,7 +113,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   _Float16 l = (_Float16)0.0f;
   float m = -INFINITY;
 
-  TileOps cur, nxt;
+  TileOps<D> cur, nxt;
   if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
   for (int tile = t_lo; tile < t_hi; tile++) {
     const int64_t k0 = (int64_t)tile * bc;
@@ -101,14 +123,22 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
     for (int tt = 0; tt < 8; tt++) {
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int st = 0; st < KSTEPS; st++) acc = mfma_fp4(cur.k[tt][st], cur.ksc[tt][st], qreg[st], qsc[st], acc);
+      for (int st = 0; st < KSTEPS; st++) {
+        const uint32_t kw = tt < 4 ? cur.ksc[st].x : cur.ksc[st].y;
+        switch (tt & 3) {
+          case 0: acc = mfma_fp4_sel<0, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+          case 1: acc = mfma_fp4_sel<1, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+          case 2: acc = mfma_fp4_sel<2, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+          default: acc = mfma_fp4_sel<3, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; i++) s[4 * tt + i] = acc[i];
     }
     float bmax = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 32; k++) {
-      const int64_t key = k0 + 32 * g + k;
+      const int64_t key = k0 + 32 * g + s_key(k);
       const bool vis = (32 * g + k < bc) && key < lk && key <= shift && live_col;
       s[k] = vis ? s[k] : -INFINITY;
       bmax = fmaxf(bmax, s[k]);
@@ -128,7 +158,13 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
       v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
-      pv = mfma_fp4(cur.v[cb], cur.vsc[cb], ph, psc, pv);
+      const uint32_t vw = cur.vsc[cb / 4];
+      switch (cb & 3) {
+        case 0: pv = mfma_fp4_sel<0, 0>(cur.v[cb], vw, ph, psc, pv); break;
+        case 1: pv = mfma_fp4_sel<1, 0>(cur.v[cb], vw, ph, psc, pv); break;
+        case 2: pv = mfma_fp4_sel<2, 0>(cur.v[cb], vw, ph, psc, pv); break;
+        default: pv = mfma_fp4_sel<3, 0>(cur.v[cb], vw, ph, psc, pv); break;
+      }
       state_update(o[cb], rs.alpha, pv);
     }
     l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
@@ -138,13 +174,22 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 
   if (!live_col) return;
   const int64_t part = ((int64_t)b * a.heads_q + h) * a.num_splits + split;
-  uint16_t* po = a.part_o + part * D;
+  // register i of block cb holds channel CB (4 g + i) + cb: CB adjacent channels per i
+  uint16_t* po = a.part_o + part * D + CB * 4 * g;
 #pragma unroll
-  for (int cb = 0; cb < CB; cb++) {
-    uint2 w;
-    w.x = __builtin_bit_cast(uint32_t, o[cb][0]);  // element 0 in the low half
-    w.y = __builtin_bit_cast(uint32_t, o[cb][1]);
-    *reinterpret_cast<uint2*>(po + 16 * cb + 4 * g) = w;
+  for (int i = 0; i < 4; i++) {
+    uint32_t w[CB / 2];
+#pragma unroll
+    for (int cb = 0; cb < CB; cb += 2) {
+      // the FP16 bits of register i: half (i & 1) of the pair o[cb][i / 2]
+      const uint32_t p0 = __builtin_bit_cast(uint32_t, o[cb][i >> 1]);
+      const uint32_t p1 = __builtin_bit_cast(uint32_t, o[cb + 1][i >> 1]);
+      const uint32_t h0 = (i & 1) ? (p0 >> 16) : (p0 & 0xFFFFu);
+      const uint32_t h1 = (i & 1) ? (p1 >> 16) : (p1 & 0xFFFFu);
+      w[cb / 2] = h0 | (h1 << 16);
+    }
+#pragma unroll
+    for (int j = 0; j < CB / 2; j += 2) *reinterpret_cast<uint2*>(po + CB * i + 2 * j) = make_uint2(w[j], w[j + 1]);
   }
   if (g == 0) {
     a.part_ml[part * 2 + 0] = __builtin_bit_cast(uint16_t, (_Float16)m);

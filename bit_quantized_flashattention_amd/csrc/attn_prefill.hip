@@ -33,6 +33,7 @@ namespace hifa4 {
 namespace {
 
 constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wave's rows)
+constexpr int kStages = 3;      // LDS ring: tiles j and j+1 resident while tile j+2 streams in
 
 template <int D>
 struct Cfg {
@@ -40,35 +41,22 @@ struct Cfg {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKSteps = D >= 128 ? D / 128 : 1;  // MFMA contractions over d
   static constexpr int kCB = D / 16;                      // 16-channel output blocks
-  // 16-byte chunks of one tile: K-hat codes (128 keys x D/2 bytes) then V-hat^T codes (D x 64)
-  static constexpr int kKChunks = kTileKeys * (D / 32);
-  static constexpr int kChunks = 2 * kKChunks;
-  static constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-  // scale dwords of one tile: K-hat (128 x D/32 bytes) then V-hat (D x 4 bytes)
-  static constexpr int kKScaleWords = kTileKeys * (D / kBlock) / 4;
-  static constexpr int kScaleWords = kKScaleWords + D;
-};
-
-// Row stride in bytes of the V-hat scale rows in LDS: one row per 32-key block, padded so that the
-// four lane groups of a wave (one block each) read four different bank ranges.
-template <int D>
-constexpr int vs_stride() { return D + 16; }
-
-// One LDS buffer: K-hat codes [128 keys][D/2] (16-byte chunks XOR-swizzled, see kswz), K-hat
-// scales transposed [D/32 blocks][128 keys], V-hat^T codes [D][64] (chunks swizzled, see vswz),
-// V-hat scales [4 blocks][D] (rows vs_stride apart).
-template <int D>
-struct Tile {
-  uint8_t kc[kTileKeys * (D / 2)];
-  uint8_t ks[kTileKeys * (D / kBlock)];
-  uint8_t vc[D * (kTileKeys / 2)];
-  uint8_t vs[4 * vs_stride<D>()];
-};
-
-template <int D>
-struct Prefetch {
-  uint4 c[Cfg<D>::kChunksPerThread];
-  uint32_t sw;  // one scale dword (threads < kScaleWords)
+  static constexpr int kKRow = D / 2;                     // bytes of one K-hat key row
+  static constexpr int kNB = D / kBlock;                  // scale blocks per key
+  // byte offsets inside one LDS stage
+  static constexpr int kKC = 0;                                   // K-hat codes [128][D/2]
+  static constexpr int kVC = kKC + kTileKeys * kKRow;             // V-hat^T codes [D][64]
+  static constexpr int kKS = kVC + D * (kTileKeys / 2);           // K-hat scales [D/32][128]
+  static constexpr int kVS = kKS + kTileKeys * kNB;               // V-hat scales [4][D]
+  static constexpr int kStageBytes = kVS + 4 * D;
+  // wave-wide loads that fill one stage: codes at 16 bytes per lane (1 KB per load), scales at
+  // 4 bytes per lane (256 bytes per load)
+  static constexpr int kKCInstr = kTileKeys * kKRow / 1024;
+  static constexpr int kVCInstr = D * (kTileKeys / 2) / 1024;
+  static constexpr int kKSInstr = kTileKeys * kNB / 256;
+  static constexpr int kVSInstr = 4 * D / 256;
+  static constexpr int kInstr = kKCInstr + kVCInstr + kKSInstr + kVSInstr;
+  static constexpr int kMaxLoadsPerWave = (kInstr + kWaves - 1) / kWaves;
 };
 
 // XOR swizzles of the 16-byte chunks inside an LDS row.  One MFMA operand read touches, per
@@ -76,6 +64,7 @@ struct Prefetch {
 // V-hat; the swizzle makes the 16-byte slots of any 8 consecutive lanes distinct modulo 128 bytes
 // and of any 16 lanes distinct modulo 256 bytes, so the read is conflict-free whether the LDS
 // serves it in 8-lane (32-bank) or 16-lane (64-bank) passes.  Both terms are fixed per lane.
+// Each is an involution: applied to a stored position it gives the chunk stored there.
 template <int D>
 __device__ __forceinline__ int kswz(int key, int chunk) {
   return D >= 128 ? chunk ^ (((key >> 5) & 3) ^ (((key >> 1) & 1) << 1)) : chunk ^ ((key >> 5) & 1);
@@ -90,81 +79,132 @@ __device__ __forceinline__ float wave_sum16(float x) {  // sum over the 16 lanes
   return x;
 }
 
-// HBM -> registers: this thread's code chunks and scale dword of the tile at key k0.  Keys at or
-// past lk (and past bc for 64-key tiles) read as code 0 with scale byte 0x7F.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// One wave-wide load of a stage: section (0 K-hat codes, 1 V-hat codes, 2 K-hat scales, 3 V-hat
+// scales), its byte offset inside the stage (the same for all lanes: the hardware writes lane i
+// at that offset + i * size) and this lane's byte offset inside the (batch, KV head) slice of
+// its section at key 0.  Positions are inverted here: a lane loads whatever HBM bytes belong at
+// its LDS position.  K-hat row R = 32a + 4t + b holds key 32a + 8b + t (the row MFMA t's lane
+// 4a + b reads, see score_row_key) and V-hat^T row R = 16cb + col holds channel CB col + cb (the
+// row PV MFMA cb's lane col reads), so each MFMA operand read is one fixed per-lane address plus
+// an immediate; the 16-byte chunks of both are XOR-swizzled (kswz, vswz).
+struct LoadOp {
+  int sec;
+  int lds;
+  int voff;
+};
+
 template <int D>
-__device__ __forceinline__ void fetch_tile(Prefetch<D>& pf, const uint8_t* kc_g, const uint8_t* ks_g,
-                                           const uint8_t* vc_g, const uint8_t* vs_g, int k0, int lk,
-                                           int lk32, int bc, int tid) {
+__device__ __forceinline__ LoadOp load_op(int i, int lane, int lk32) {
   using C = Cfg<D>;
-  constexpr int CPR = D / 32;  // 16-byte chunks per K-hat key row
-#pragma unroll
-  for (int i = 0; i < C::kChunksPerThread; i++) {
-    const int c = tid + i * C::kThreads;
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (c < C::kKChunks) {
-      const int r = c / CPR, part = c % CPR;
-      if (r < bc && k0 + r < lk) w = *reinterpret_cast<const uint4*>(kc_g + (int64_t)(k0 + r) * (D / 2) + 16 * part);
-    } else if (c < C::kChunks) {
-      const int cv = c - C::kKChunks;  // (32-key block, channel): 16 bytes, contiguous in HBM
-      const int part = cv / D, ch = cv % D;
-      if (32 * part < bc && k0 + 32 * part < lk32)
-        w = *reinterpret_cast<const uint4*>(vc_g + ((int64_t)(k0 / kBlock + part) * D + ch) * 16);
-    }
-    pf.c[i] = w;
+  LoadOp op;
+  if (i < C::kKCInstr) {
+    const int pos = i * 1024 + 16 * lane;
+    const int r = pos / C::kKRow, p = (pos % C::kKRow) / 16;
+    const int c = D >= 128 ? ((p & ~3) | kswz<D>(r, p & 3)) : kswz<D>(r, p);
+    const int key = 32 * (r >> 5) + 8 * (r & 3) + ((r >> 2) & 7);
+    op.sec = 0;
+    op.lds = C::kKC + i * 1024;
+    op.voff = key * C::kKRow + 16 * c;
+  } else if (i < C::kKCInstr + C::kVCInstr) {
+    const int q = i - C::kKCInstr;
+    const int pos = q * 1024 + 16 * lane;
+    const int r = pos / 64, part = vswz(r, (pos % 64) / 16);
+    const int ch = C::kCB * (r % 16) + r / 16;
+    op.sec = 1;
+    op.lds = C::kVC + q * 1024;
+    op.voff = (part * D + ch) * 16;  // block-major V-hat: (32-key block, channel) cells
+  } else if (i < C::kKCInstr + C::kVCInstr + C::kKSInstr) {
+    const int q = i - C::kKCInstr - C::kVCInstr;
+    const int pos = q * 256 + 4 * lane;  // [block][key] rows of 128 bytes
+    op.sec = 2;
+    op.lds = C::kKS + q * 256;
+    op.voff = (pos / kTileKeys) * lk32 + pos % kTileKeys;
+  } else {
+    const int q = i - C::kKCInstr - C::kVCInstr - C::kKSInstr;
+    op.sec = 3;
+    op.lds = C::kVS + q * 256;
+    op.voff = q * 256 + 4 * lane;  // 4 blocks x D channels, contiguous
   }
-  uint32_t w = 0x7F7F7F7Fu;
-  if (tid < C::kKScaleWords) {
-    const int c = tid * 4;  // first scale byte of the dword: key c / (D/32), block c % (D/32)
-    const int r = c / (D / kBlock);
-    if (D >= 128) {
-      if (r < bc && k0 + r < lk) w = *reinterpret_cast<const uint32_t*>(ks_g + (int64_t)(k0 + r) * (D / kBlock) + c % (D / kBlock));
-    } else {  // D = 64: two keys per dword
-      uint32_t lo = 0x7F7Fu, hi = 0x7F7Fu;
-      if (r < bc && k0 + r < lk) lo = *reinterpret_cast<const uint16_t*>(ks_g + (int64_t)(k0 + r) * 2);
-      if (r + 1 < bc && k0 + r + 1 < lk) hi = *reinterpret_cast<const uint16_t*>(ks_g + (int64_t)(k0 + r + 1) * 2);
-      w = lo | (hi << 16);
-    }
-  } else if (tid < C::kScaleWords) {
-    // V-hat scales of the tile: 4 blocks x D channels, contiguous in HBM; dword j holds channels
-    // 4j % D .. +3 of block 4j / D
-    const int j = tid - C::kKScaleWords;
-    const int part = 4 * j / D;
-    if (32 * part < bc && k0 + 32 * part < lk32)
-      w = *reinterpret_cast<const uint32_t*>(vs_g + (int64_t)(k0 / kBlock) * D + 4 * j);
-  }
-  pf.sw = w;
+  return op;
 }
 
-// registers -> LDS buffer (swizzled codes, transposed K-hat scales)
+// Raw buffer descriptor (stride 0) of one (batch, KV head) slice of a section: a load past the
+// end of the slice returns zeros (codes 0 and scale byte 0, i.e. 2^-127), which is what the
+// ragged tail of the last tile needs.
+__device__ __forceinline__ v4i make_desc(const void* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  v4i d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
+  d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  d[3] = 0x00020000;
+  return d;
+}
+
+struct Slices {
+  v4i r[4];
+};
+
+// LDS byte address of a pointer into the work-group's shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// HBM -> LDS without registers: each lane's SIZE bytes at voff (+ the descriptor's base) land at
+// LDS address m0 + lane * SIZE.  The load is tracked by the wave's vector-memory counter only;
+// the kernel waits for it explicitly (wait_vmem) before the barrier that publishes the stage.
+template <int SIZE>
+__device__ __forceinline__ void dma(const v4i& desc, uint32_t lds, int voff) {
+  if (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(desc)
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(desc)
+                 : "m0");
+}
+
+// Issue this wave's n loads of the tile starting at key k0 into the stage at LDS address stage.
 template <int D>
-__device__ __forceinline__ void store_tile(Tile<D>& t, const Prefetch<D>& pf, int tid) {
+__device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, int n, uint32_t stage, int k0) {
   using C = Cfg<D>;
-  constexpr int CPR = D / 32;
 #pragma unroll
-  for (int i = 0; i < C::kChunksPerThread; i++) {
-    const int c = tid + i * C::kThreads;
-    if (c < C::kKChunks) {
-      const int r = c / CPR, part = c % CPR;
-      const int sw = (part & ~3) | kswz<D>(r, part & 3);
-      *reinterpret_cast<uint4*>(&t.kc[r * (D / 2) + 16 * sw]) = pf.c[i];
-    } else if (c < C::kChunks) {
-      const int cv = c - C::kKChunks;
-      const int part = cv / D, ch = cv % D;
-      *reinterpret_cast<uint4*>(&t.vc[ch * 64 + 16 * vswz(ch, part)]) = pf.c[i];
-    }
+  for (int i = 0; i < C::kMaxLoadsPerWave; i++) {
+    if (i >= n) break;
+    const LoadOp& op = ops[i];
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);  // uniform: m0
+    // the whole offset goes in the per-lane operand, which is what the range check covers
+    if (op.sec == 0) dma<16>(sl.r[0], dst, op.voff + k0 * C::kKRow);
+    else if (op.sec == 1) dma<16>(sl.r[1], dst, op.voff + k0 * C::kKRow);
+    else if (op.sec == 2) dma<4>(sl.r[2], dst, op.voff + k0);
+    else dma<4>(sl.r[3], dst, op.voff + (k0 / kBlock) * D);
   }
-  if (tid < C::kKScaleWords) {  // 4 scale bytes -> transposed [block][key]
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int c = tid * 4 + j;
-      const int key = D >= 128 ? c / (D / kBlock) : c / 2;
-      const int blk = D >= 128 ? c % (D / kBlock) : c % 2;
-      t.ks[blk * kTileKeys + key] = (uint8_t)(pf.sw >> (8 * j));
+}
+
+// s_waitcnt for "at most N vector-memory operations of this wave outstanding" (gfx9 encoding;
+// the other counters are left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// the same for a wave-uniform n <= MAX (the waves of a work-group issue different numbers of loads)
+template <int MAX>
+__device__ __forceinline__ void wait_vmem_n(int n) {
+  if constexpr (MAX > 0) {
+    if (n >= MAX) {
+      wait_vmem<MAX>();
+      return;
     }
-  } else if (tid < C::kScaleWords) {
-    const int j = tid - C::kKScaleWords;
-    *reinterpret_cast<uint32_t*>(&t.vs[(4 * j / D) * vs_stride<D>() + (4 * j) % D]) = pf.sw;
+    wait_vmem_n<MAX - 1>(n);
+  } else {
+    wait_vmem<0>();
   }
 }
 
@@ -174,7 +214,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
   constexpr int W = Cf::kWaves;
   constexpr int KSTEPS = Cf::kKSteps;
   constexpr int CB = Cf::kCB;
-  __shared__ Tile<D> tiles[2];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * Cf::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,6 +253,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
     }
   }
 
+  // the Q-hat loads complete here, so no wait for them lands inside the tile loop
+  wait_vmem<0>();
+
   // ---- FP16 state; m is an integer-valued float
   h2 o[CB][2];
 #pragma unroll
@@ -236,35 +279,53 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
     for (int i = lane; i < a.n_tiles * 2; i += 64) stats_row[i] = 0.0f;
   }
 
-  const uint8_t* kc_g = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * (int64_t)lk * (D / 2);
-  const uint8_t* ks_g = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * (int64_t)lk * (D / kBlock);
-  const uint8_t* vc_g = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / 2);
-  const uint8_t* vs_g = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * (int64_t)D * (lk32 / kBlock);
-  // (both are the start of this (batch, KV head)'s block-major V-hat: lk32/32 blocks of D cells)
+  const int64_t slice = (int64_t)b * a.heads_kv + kvh;
+  Slices sl;
+  sl.r[0] = make_desc(a.k_codes + slice * lk * (D / 2), (int64_t)lk * (D / 2));
+  sl.r[1] = make_desc(a.v_codes + slice * lk32 * (D / 2), (int64_t)lk32 * (D / 2));
+  sl.r[2] = make_desc(a.k_scales + slice * (D / kBlock) * lk32, (int64_t)(D / kBlock) * lk32);
+  sl.r[3] = make_desc(a.v_scales + slice * (lk32 / kBlock) * D, (int64_t)(lk32 / kBlock) * D);
+  const uint32_t smem_lds = lds_addr(smem);
+  // this wave's share of the stage loads: instructions wave, wave + W, ...
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int n_loads = wave_u < Cf::kInstr ? (Cf::kInstr - wave_u + W - 1) / W : 0;
+  LoadOp ops[Cf::kMaxLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < Cf::kMaxLoadsPerWave; i++) ops[i] = load_op<D>(wave_u + W * i, lane, lk32);
   const float C = a.c_log2;
 
-  // per-lane LDS offsets of this lane's MFMA operands (see the loads in the tile loop)
-  const int k_lane_off = (32 * (col >> 2) + (col & 3)) * (D / 2) + 16 * kswz<D>(32 * (col >> 2) + (col & 3), g);
-  const int ks_lane_off = g * kTileKeys + 32 * (col >> 2) + (col & 3);
-  const int v_lane_off = col * 64 + 16 * vswz(col, g);
-  const int vs_lane_off = g * vs_stride<D>() + col;
+  // per-lane LDS offsets of this lane's MFMA operands (see the reads in the tile loop)
+  const int k_lane_off = Cf::kKC + (32 * (col >> 2) + (col & 3)) * (D / 2) + 16 * kswz<D>(32 * (col >> 2) + (col & 3), g);
+  const int ks_lane_off = Cf::kKS + g * kTileKeys + 32 * (col >> 2) + 8 * (col & 3);
+  const int v_lane_off = Cf::kVC + col * 64 + 16 * vswz(col, g);
+  const int vs_lane_off = Cf::kVS + g * D + CB * col;
 
-  Prefetch<D> pf;
-  fetch_tile<D>(pf, kc_g, ks_g, vc_g, vs_g, 0, lk, lk32, bc, tid);
-  store_tile<D>(tiles[0], pf, tid);
+  // prologue: tiles 0 .. kStages-2 in flight, wait for tile 0
+#pragma unroll
+  for (int p = 0; p < kStages - 1; p++)
+    if (p < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
+  if (n_tiles > 1) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
+  else wait_vmem<0>();
   __syncthreads();
 
   for (int tile = 0; tile < n_tiles; tile++) {
     const int k0 = tile * bc;
-    const Tile<D>& T = tiles[tile & 1];
-    if (tile + 1 < n_tiles) fetch_tile<D>(pf, kc_g, ks_g, vc_g, vs_g, k0 + bc, lk, lk32, bc, tid);
+    const uint8_t* T = smem + (tile % kStages) * Cf::kStageBytes;
+    const int ahead = tile + kStages - 1;
+    if (ahead < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
 
     if (wave_live && !(CAUSAL && k0 > wave_last + shift)) {
       // ---- S^T = K-hat Q-hat^T: MFMA t reads key kr = 32 (col/4) + 4t + (col%4); the per-lane
       // part is a fixed base, t and the contraction step are immediate offsets (the swizzle term
       // kr/32 = col/4 does not depend on t).  Lane holds keys k0 + 32 g + (4 t + i).
-      const uint8_t* kbase = T.kc + k_lane_off;
-      const uint8_t* ksbase = T.ks + ks_lane_off;
+      const uint8_t* kbase = T + k_lane_off;
+      // the lane's 8 K-hat scale bytes of each contraction step (byte t serves MFMA t)
+      uint2 ksw[KSTEPS];
+#pragma unroll
+      for (int st = 0; st < KSTEPS; st++) {
+        ksw[st] = *reinterpret_cast<const uint2*>(T + ks_lane_off + 4 * kTileKeys * st);
+        if (D < 128 && g >= 2) ksw[st] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      }
       float s[32];
 #pragma unroll
       for (int t = 0; t < 8; t++) {
@@ -272,12 +333,14 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
 #pragma unroll
         for (int st = 0; st < KSTEPS; st++) {
           uint4 ka = make_uint4(0u, 0u, 0u, 0u);
-          uint32_t ksc = 127u;
-          if (D >= 128 || g < 2) {
-            ka = *reinterpret_cast<const uint4*>(kbase + 4 * t * (D / 2) + 64 * st);
-            ksc = ksbase[4 * t + 4 * st * kTileKeys];
+          if (D >= 128 || g < 2) ka = *reinterpret_cast<const uint4*>(kbase + 4 * t * (D / 2) + 64 * st);
+          const uint32_t kw = t < 4 ? ksw[st].x : ksw[st].y;
+          switch (t & 3) {
+            case 0: acc = mfma_fp4_sel<0, 0>(ka, kw, qreg[st], qsc[st], acc); break;
+            case 1: acc = mfma_fp4_sel<1, 0>(ka, kw, qreg[st], qsc[st], acc); break;
+            case 2: acc = mfma_fp4_sel<2, 0>(ka, kw, qreg[st], qsc[st], acc); break;
+            default: acc = mfma_fp4_sel<3, 0>(ka, kw, qreg[st], qsc[st], acc); break;
           }
-          acc = mfma_fp4(ka, ksc, qreg[st], qsc[st], acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) s[4 * t + i] = acc[i];
@@ -297,7 +360,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
         if (q >= lq) lim = -1;
 #pragma unroll
         for (int k = 0; k < 32; k++) {
-          s[k] = (kb + k <= lim) ? s[k] : -INFINITY;
+          s[k] = (kb + s_key(k) <= lim) ? s[k] : -INFINITY;
           bmax = fmaxf(bmax, s[k]);
         }
       }
@@ -330,38 +393,50 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
       }
       // ---- O^T += V-hat^T P-hat^T per 16-channel block (channel 16 cb + col; the swizzle term
       // (ch/4)%4 = col/4); FP16 state update
-      const uint8_t* vbase = T.vc + v_lane_off;
-      const uint8_t* vsbase = T.vs + vs_lane_off;
+      const uint8_t* vbase = T + v_lane_off;
+      // the lane's CB V-hat scale bytes (byte cb serves channel block cb)
+      uint32_t vsw[CB / 4];
+      if constexpr (CB == 4) {
+        vsw[0] = *reinterpret_cast<const uint32_t*>(T + vs_lane_off);
+      } else if constexpr (CB == 8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(T + vs_lane_off);
+        vsw[0] = w.x;
+        vsw[1] = w.y;
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(T + vs_lane_off);
+        vsw[0] = w.x;
+        vsw[1] = w.y;
+        vsw[2] = w.z;
+        vsw[3] = w.w;
+      }
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
         const uint4 va = *reinterpret_cast<const uint4*>(vbase + 16 * 64 * cb);
-        const uint32_t vsc = vsbase[16 * cb];
+        const uint32_t vw = vsw[cb / 4];
         v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
-        pv = mfma_fp4(va, vsc, ph, psc, pv);
+        switch (cb & 3) {
+          case 0: pv = mfma_fp4_sel<0, 0>(va, vw, ph, psc, pv); break;
+          case 1: pv = mfma_fp4_sel<1, 0>(va, vw, ph, psc, pv); break;
+          case 2: pv = mfma_fp4_sel<2, 0>(va, vw, ph, psc, pv); break;
+          default: pv = mfma_fp4_sel<3, 0>(va, vw, ph, psc, pv); break;
+        }
         state_update(o[cb], rs.alpha, pv);
       }
       l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
       m = rs.m_new;
     }
 
-    if (tile + 1 < n_tiles) store_tile<D>(tiles[(tile + 1) & 1], pf, tid);
+    // tile + 1 must be resident before the barrier; the loads of tile + 2 may stay in flight
+    if (tile + 2 < n_tiles) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
+    else wait_vmem<0>();
     __syncthreads();
   }
 
-  // ---- epilogue: out = fp16(O / l); lane holds channels 16 cb + 4 g + i of its query
+  // ---- epilogue: out = fp16(O / l); register i of block cb holds channel CB (4 g + i) + cb
   const int q = q0 + col;
   if (!wave_live || q >= lq) return;
   uint16_t* out = a.out + ((int64_t)b * a.heads_q + h) * (int64_t)lq * D;
-  const float lv = (float)l;
-#pragma unroll
-  for (int cb = 0; cb < CB; cb++) {
-    const h2 r01 = h2{(_Float16)((float)o[cb][0][0] / lv), (_Float16)((float)o[cb][0][1] / lv)};
-    const h2 r23 = h2{(_Float16)((float)o[cb][1][0] / lv), (_Float16)((float)o[cb][1][1] / lv)};
-    uint2 w;
-    w.x = __builtin_bit_cast(uint32_t, r01);
-    w.y = __builtin_bit_cast(uint32_t, r23);
-    *reinterpret_cast<uint2*>(out + (int64_t)q * D + 16 * cb + 4 * g) = w;
-  }
+  write_out_row<CB>(out + (int64_t)q * D + CB * 4 * g, o, (float)l);
 }
 
 int gcd_int(int x, int y) {

@@ -113,9 +113,26 @@ __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   return r;
 }
 
+// Key and channel maps of the 16x16x128 MFMAs (all offsets inside one 128-key tile).
+//
+// Scores are computed transposed, S^T = K-hat Q-hat^T, with the 16 MFMA columns = 16 queries.
+// Score MFMA t (t = 0..7) takes key kappa(t, r) = 32 (r/4) + 8 (r%4) + t as its row r; its output
+// register i of lane group g then holds key 32 g + 8 i + t, so after the 8 MFMAs lane (g, col)
+// holds all 32 keys of block g of its query (s[4 t + i]), the slice the PV MFMA consumes as its
+// B operand, and the 8 keys whose scales row r = col needs (t = 0..7) are adjacent.
+__device__ __forceinline__ int score_row_key(int t, int r) { return 32 * (r >> 2) + 8 * (r & 3) + t; }
+// key offset (inside the lane group's 32-key block) of accumulator value s[k]
+__device__ __host__ constexpr int s_key(int k) { return 8 * (k & 3) + (k >> 2); }
+// accumulator index holding key offset j of the block
+__device__ __host__ constexpr int s_index(int j) { return 4 * (j & 7) + (j >> 3); }
+// PV MFMA cb takes channel chi(cb, r) = CB r + cb as its row r, so lane (g, col) needs the scales
+// of channels CB col .. CB col + CB - 1 (adjacent) and its output register i holds channel
+// CB (4 g + i) + cb of its query.
+
 // P-hat codes of a lane's 32 keys: E2M1 of rn16(2^rn16(fma32(s_k, C, -(m + e)))), packed two
-// per byte, key 2j in the low nibble; a score of -inf (masked key) gives the code 0.  The FP16
-// probabilities are left in p16 (pairs) for callers that sum them.
+// per byte in key order (key 2j of the block in the low nibble of byte j); a score of -inf
+// (masked key) gives the code 0.  The FP16 probabilities are left in p16 (pairs of keys
+// (2j, 2j + 1)) for callers that sum them.
 __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, uint32_t* p16) {
   uint32_t w[4];
 #pragma unroll
@@ -123,9 +140,9 @@ __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, 
     uint32_t x = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const int k = 8 * q + 2 * j;
-      const float u0 = keep_f32(__builtin_fmaf(s[k], C, nbm));
-      const float u1 = keep_f32(__builtin_fmaf(s[k + 1], C, nbm));
+      const int k = 8 * q + 2 * j;  // key offsets k, k + 1
+      const float u0 = keep_f32(__builtin_fmaf(s[s_index(k)], C, nbm));
+      const float u1 = keep_f32(__builtin_fmaf(s[s_index(k + 1)], C, nbm));
       const uint32_t pr = exp2_h2(pack_h2(u0, u1));
       p16[k / 2] = pr;
       if (j == 0) x = cvt_fp4x2_h<0>(x, pr);
@@ -163,6 +180,30 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
   o[1] = __builtin_elementwise_fma(a2, o[1], __builtin_bit_cast(h2, pack_h2(pv[2], pv[3])));
 }
 
+// Writes one query's output row fp16(O / l) from the FP16 state of CB channel blocks: register i
+// (i = 0..3) of block cb holds channel CB (4 g + i) + cb, so for each i the CB values are
+// adjacent channels; dst points at channel 4 g CB of the row.
+template <int CB>
+__device__ __forceinline__ void write_out_row(uint16_t* dst, const h2 (*o)[2], float l) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    uint32_t w[CB / 2];
+#pragma unroll
+    for (int cb = 0; cb < CB; cb += 2) {
+      const float x0 = (float)o[cb][i >> 1][i & 1] / l;
+      const float x1 = (float)o[cb + 1][i >> 1][i & 1] / l;
+      w[cb / 2] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+    }
+    uint16_t* d = dst + CB * i;
+    if constexpr (CB == 4) {
+      *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CB / 2; j += 4) *reinterpret_cast<uint4*>(d + 2 * j) = make_uint4(w[j], w[j + 1], w[j + 2], w[j + 3]);
+    }
+  }
+}
+
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, uint32_t sa, const uint4& b, uint32_t sb,
                                          v4f c) {
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -170,6 +211,15 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, uint32_t sa, const uint4
   // cbsz = blgp = 4: both operands E2M1; byte 0 of sa / sb is the E8M0 scale of this lane's
   // 32-element block.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// The same with the scale bytes taken from byte SA of sa and byte SB of sb (the instruction's
+// scale-select fields), so four scales packed in one register need no unpacking.
+template <int SA, int SB>
+__device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, uint32_t sa, const uint4& b, uint32_t sb, v4f c) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SA, (int)sa, SB, (int)sb);
 }
 
 // Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950 row-swap

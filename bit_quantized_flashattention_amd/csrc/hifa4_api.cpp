@@ -179,15 +179,15 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
   const int group = dims->heads_q / dims->heads_kv;
   if (q) {
     hifa4::QuantRowsArgs a{(const uint16_t*)q, s, (int64_t)dims->batch * dims->heads_q * dims->len_q,
-                           dims->len_q, dims->heads_q, group, dims->head_dim, (uint8_t*)q_codes,
-                           (uint8_t*)q_scales};
+                           dims->len_q, round32(dims->len_q), dims->heads_q, group, dims->head_dim, 0,
+                           (uint8_t*)q_codes, (uint8_t*)q_scales};
     hipError_t e = hifa4::launch_quantize_rows(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
   }
   if (k) {
     hifa4::QuantRowsArgs a{(const uint16_t*)k, inv_s, (int64_t)dims->batch * dims->heads_kv * dims->len_kv,
-                           dims->len_kv, dims->heads_kv, 1, dims->head_dim, (uint8_t*)k_codes,
-                           (uint8_t*)k_scales};
+                           dims->len_kv, round32(dims->len_kv), dims->heads_kv, 1, dims->head_dim, 1,
+                           (uint8_t*)k_codes, (uint8_t*)k_scales};
     hipError_t e = hifa4::launch_quantize_rows(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
   }

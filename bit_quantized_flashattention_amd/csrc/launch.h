@@ -11,11 +11,13 @@ struct QuantRowsArgs {
   const float* scale;   // FP32 [Hs, d] or nullptr
   int64_t rows;         // B * H * L
   int64_t len;          // L
+  int64_t len32;        // L rounded up to 32 (block-plane scales)
   int32_t heads;        // H
   int32_t heads_per_scale_row;  // query heads per KV head for Q (Hq/Hkv), 1 for K
   int32_t d;
+  int32_t block_planes; // 0: scales [rows, d/32] (Q-hat); 1: [B*H, d/32, len32] (K-hat), tail 0
   uint8_t* codes;       // [rows, d/2]
-  uint8_t* scales;      // [rows, d/32]
+  uint8_t* scales;
 };
 
 struct QuantVtArgs {

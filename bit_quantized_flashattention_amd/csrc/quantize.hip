@@ -9,13 +9,29 @@ namespace hifa4 {
 
 // One thread per 32-element block along d: 64 B of FP16 in, 16 B of codes + 1 scale byte out.
 // Consecutive threads own consecutive blocks, so loads and stores are contiguous per wave.
-template <int D>
+// K-hat scales are written as block planes [B*H, d/32, len32] (one row of key scales per
+// 32-channel block, what the attention kernels stage per tile); threads past the last key of
+// a row write the zero scale bytes of the padding.
+template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   constexpr int NB = D / kBlock;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.rows * NB) return;
-  const int64_t row = t / NB;
+  const int64_t n_rows = PLANES ? a.rows / a.len * a.len32 : a.rows;
+  if (t >= n_rows * NB) return;
   const int blk = (int)(t % NB);
+  int64_t row = t / NB;
+  uint8_t* scale_dst;
+  if (PLANES) {
+    const int64_t bh = row / a.len32, tok = row % a.len32;
+    scale_dst = a.scales + (bh * NB + blk) * a.len32 + tok;
+    if (tok >= a.len) {
+      *scale_dst = 0;
+      return;
+    }
+    row = bh * a.len + tok;
+  } else {
+    scale_dst = a.scales + row * NB + blk;
+  }
   const uint4* src = reinterpret_cast<const uint4*>(a.x + row * D + blk * kBlock);
   uint4 raw[4];
 #pragma unroll
@@ -55,7 +71,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   out.z = pack8_fp4(v + 16, sc);
   out.w = pack8_fp4(v + 24, sc);
   *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + blk * 16) = out;
-  a.scales[row * NB + blk] = (uint8_t)(e + 127);
+  *scale_dst = (uint8_t)(e + 127);
 }
 
 // V: blocks run along tokens, so a work-group stages 128 tokens x d channels in LDS and each
@@ -108,9 +124,11 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
 
 template <int D>
 static hipError_t quant_rows_d(const QuantRowsArgs& a, hipStream_t s) {
-  const int64_t items = a.rows * (D / kBlock);
+  const int64_t rows = a.block_planes ? a.rows / a.len * a.len32 : a.rows;
+  const int64_t items = rows * (D / kBlock);
   const int64_t grid = (items + 255) / 256;
-  hipLaunchKernelGGL(quantize_rows_kernel<D>, dim3((uint32_t)grid), dim3(256), 0, s, a);
+  if (a.block_planes) hipLaunchKernelGGL((quantize_rows_kernel<D, true>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((quantize_rows_kernel<D, false>), dim3((uint32_t)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

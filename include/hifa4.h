@@ -16,7 +16,9 @@
  * Memory layouts (all row-major, contiguous, no padding between rows):
  *   q        FP16 [B, Hq,  Lq, d]            k, v      FP16 [B, Hkv, Lk, d]
  *   q_codes  u8   [B, Hq,  Lq, d/2]          q_scales  u8   [B, Hq,  Lq, d/32]
- *   k_codes  u8   [B, Hkv, Lk, d/2]          k_scales  u8   [B, Hkv, Lk, d/32]
+ *   k_codes  u8   [B, Hkv, Lk, d/2]          k_scales  u8   [B, Hkv, d/32, Lk32]
+ *                 (K-hat scales are block planes: for each 32-channel block, the scale bytes of
+ *                 all keys; bytes of the padding keys Lk .. Lk32-1 are 0)
  *   v_codes  u8   [B, Hkv, Lk32/32, d, 16]   v_scales  u8   [B, Hkv, Lk32/32, d]
  *                 (V-hat is blocked along tokens and stored block-major: for each block of 32
  *                 tokens, the 16 code bytes of channel 0, then channel 1, ...; a key tile is one

@@ -136,15 +136,20 @@ class Quantized:
     def packed(self):
         """Bytes in the library's HBM layout: (q_codes, q_scales, k_codes, k_scales, v_codes, v_scales).
 
-        Q-hat and K-hat are row-major as computed.  V-hat is stored token-block major: for each
-        32-token block, the 16 code bytes of every channel ([B, Hkv, Lk32/32, d, 16]) and the
-        scale bytes of every channel ([B, Hkv, Lk32/32, d]).
+        Q-hat and K-hat codes and the Q-hat scales are row-major as computed.  The K-hat scales
+        are stored as block planes: for each 32-channel block, the scale bytes of all keys,
+        padded with zero bytes to a multiple of 32 keys ([B, Hkv, d/32, Lk32]).  V-hat is stored
+        token-block major: for each 32-token block, the 16 code bytes of every channel
+        ([B, Hkv, Lk32/32, d, 16]) and the scale bytes of every channel ([B, Hkv, Lk32/32, d]).
         """
         b, hkv, d, lk32 = self.vc.shape
+        lk = self.kc.shape[2]
         vcode = mx.pack_codes(self.vc).reshape(b, hkv, d, lk32 // 32, 16).transpose(0, 1, 3, 2, 4)
         vscale = np.swapaxes(mx.scale_bytes(self.ve), 2, 3)
+        kscale = np.zeros((b, hkv, d // 32, lk32), dtype=np.uint8)
+        kscale[..., :lk] = np.swapaxes(mx.scale_bytes(self.ke), 2, 3)
         return (mx.pack_codes(self.qc), mx.scale_bytes(self.qe), mx.pack_codes(self.kc),
-                mx.scale_bytes(self.ke), np.ascontiguousarray(vcode), np.ascontiguousarray(vscale))
+                kscale, np.ascontiguousarray(vcode), np.ascontiguousarray(vscale))
 
 
 def quantize_qkv(q, k, v, s32=None, inv32=None):
