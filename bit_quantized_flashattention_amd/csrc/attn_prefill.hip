@@ -33,11 +33,14 @@ namespace hifa4 {
 namespace {
 
 constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wave's rows)
-constexpr int kStages = 3;      // LDS ring: tiles j and j+1 resident while tile j+2 streams in
+#ifndef PREFILL_STAGES
+#define PREFILL_STAGES 2
+#endif
+constexpr int kStages = PREFILL_STAGES;  // LDS ring depth (2: tile j+1 streams in while j is used)
 
 template <int D>
 struct Cfg {
-  static constexpr int kWaves = D >= 256 ? 8 : 16;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKSteps = D >= 128 ? D / 128 : 1;  // MFMA contractions over d
   static constexpr int kCB = D / 16;                      // 16-channel output blocks
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
 #pragma unroll
   for (int p = 0; p < kStages - 1; p++)
     if (p < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
-  if (n_tiles > 1) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
+  if (kStages > 2 && n_tiles > 1) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
   else wait_vmem<0>();
   __syncthreads();
 
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
     }
 
     // tile + 1 must be resident before the barrier; the loads of tile + 2 may stay in flight
-    if (tile + 2 < n_tiles) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
+    if (kStages > 2 && tile + 2 < n_tiles) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
     else wait_vmem<0>();
     __syncthreads();
   }
