@@ -33,6 +33,9 @@ namespace hifa4 {
 namespace {
 
 constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wave's rows)
+#ifndef PREFILL_WAVES
+#define PREFILL_WAVES 8  // waves per work-group: 8 x 16 query rows
+#endif
 #ifndef PREFILL_STAGES
 #define PREFILL_STAGES 2
 #endif
@@ -40,7 +43,7 @@ constexpr int kStages = PREFILL_STAGES;  // LDS ring depth (2: tile j+1 streams 
 
 template <int D>
 struct Cfg {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = PREFILL_WAVES;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKSteps = D >= 128 ? D / 128 : 1;  // MFMA contractions over d
   static constexpr int kCB = D / 16;                      // 16-channel output blocks

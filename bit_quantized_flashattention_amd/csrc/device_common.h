@@ -183,15 +183,29 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
 // Writes one query's output row fp16(O / l) from the FP16 state of CB channel blocks: register i
 // (i = 0..3) of block cb holds channel CB (4 g + i) + cb, so for each i the CB values are
 // adjacent channels; dst points at channel 4 g CB of the row.
+//
+// The quotient: fp16(x / l) for FP16 values x and l > 0 equals the FP16 rounding of the IEEE
+// FP32 quotient.  Here q = x r with r ~ 1/l (hardware reciprocal, ~1 ulp) is corrected once with
+// the exact residual fma(-l, q, x), which leaves q within 0.5 ulp (FP32) plus O(2^-45) of x / l;
+// a quotient of two FP16 values is never an FP16 rounding midpoint (a midpoint has 12
+// significant bits) and stays at least 2^-22 (relative) away from one, so both round to the same
+// FP16 value.  The sign is copied from x (the quotient of -0 is -0).
+__device__ __forceinline__ float quot_h(float x, float l, float r) {
+  const float q = x * r;
+  const float e = __builtin_fmaf(-l, q, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
+}
+
 template <int CB>
 __device__ __forceinline__ void write_out_row(uint16_t* dst, const h2 (*o)[2], float l) {
+  const float r = __builtin_amdgcn_rcpf(l);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     uint32_t w[CB / 2];
 #pragma unroll
     for (int cb = 0; cb < CB; cb += 2) {
-      const float x0 = (float)o[cb][i >> 1][i & 1] / l;
-      const float x1 = (float)o[cb + 1][i >> 1][i & 1] / l;
+      const float x0 = quot_h((float)o[cb][i >> 1][i & 1], l, r);
+      const float x1 = quot_h((float)o[cb + 1][i >> 1][i & 1], l, r);
       w[cb / 2] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
     }
     uint16_t* d = dst + CB * i;
