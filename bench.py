@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 FP4_PEAK_TFLOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_BYTES = 512 << 20  # plain device copy run by --traffic-probe to calibrate the counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["attn_prefill.hip", "attn_decode.hip", "device_common.h", "quantize.hip"]
 
 
 def parse():
@@ -39,7 +42,53 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
     p.add_argument("--workload", default="prefill", choices=["prefill", "prefill-d256", "prefill-L2048"])
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="also run one plain %d MiB device copy (counter calibration for HBM traffic)"
+                        % (COPY_PROBE_BYTES >> 20))
     return p.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources: the HBM-traffic figures are valid only for these bytes."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_flashattention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(key):
+    """HBM bytes per launch of a kernel from the committed counter summary, or None.
+
+    profiles/traffic.json holds FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of each kernel and
+    of a plain copy of known size measured in the same runs; each counter is scaled by
+    bytes_copied / counter(copy).  The figures are dropped when the kernel sources changed
+    since they were taken.
+    """
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest() or key not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][key]
+    cp = t["copy"]
+    f_scale = cp["bytes"] / (cp["fetch_kib"] * 1024.0)
+    w_scale = cp["bytes"] / (cp["write_kib"] * 1024.0)
+    return int(round(k["fetch_kib"] * 1024.0 * f_scale + k["write_kib"] * 1024.0 * w_scale))
+
+
+def copy_probe():
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def causal_pairs(lq, lk):
@@ -146,7 +195,7 @@ def bench_decode(args):
         "bytes_per_step": total,
         "roofline": {"bound": "hbm", "achieved": round(total / (attn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(total / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel_us": round(attn_ms * 1e3, 1)},
+                     "traffic": traffic_for("decode"), "kernel_us": round(attn_ms * 1e3, 1)},
     }
     del qkv, ws, out, q
     torch.cuda.empty_cache()
@@ -221,7 +270,7 @@ def main():
             "head_dim": cfg["d"], "normalizer": "p_reordered", "smooth_qk_gate": pre["gate"],
         },
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": traffic_for("prefill"),
                      "kernel_ms": round(pre["attn_ms"], 4)},
     }
     if not args.no_cpu_baseline:
@@ -230,6 +279,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = bench_decode(args)
+    if args.traffic_probe:
+        copy_probe()
     print(json.dumps(line), flush=True)
 
 
