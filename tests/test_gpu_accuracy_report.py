@@ -1,0 +1,99 @@
+"""Accuracy report of the batched causal prefill (B8, L4096, Hq32/Hkv8, d128) on the GPU.
+
+[HiFA4] Abstract, Theorem 1: with l taken from the higher-precision probabilities (the
+inconsistent formulation) and O from P-hat V, every channel of a row is scaled by the same
+factor; the abstract measures the per-tile error epsilon = sum(P-hat)/sum(P) - 1 as a net
+probability-mass loss.  This test runs the full workload twice through the C ABI, P-Reordered
+and inconsistent, with per-(16-row block, tile) statistics, and reports:
+
+* epsilon over all visited tiles (median, mean, p5, p95, fraction below 0); m does not depend on
+  l, so both runs must produce identical tile sums;
+* the error of both outputs against unquantized FP32 softmax attention (oracle.reference_fp32 on
+  the original FP16 inputs) on sampled heads.
+
+The magnitude of epsilon has no value on the pages for synthetic inputs (parity unpinned); the
+test checks the sign the abstract reports and that the tile sums of the two runs agree.  Set
+HIFA4_REPORT to a file path to keep the report as JSON.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bit_quantized_flashattention_amd as hf
+from oracle import attention as A
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _eps_stats(st):
+    sph = st[..., 0].astype(np.float64)
+    sp = st[..., 1].astype(np.float64)
+    vis = sp > 0
+    eps = sph[vis] / sp[vis] - 1.0
+    return eps, {
+        "tiles": int(vis.sum()),
+        "median": float(np.median(eps)), "mean": float(np.mean(eps)),
+        "p5": float(np.percentile(eps, 5)), "p95": float(np.percentile(eps, 95)),
+        "frac_below_0": float(np.mean(eps < 0)),
+    }
+
+
+def test_accuracy_report_batched_prefill():
+    import torch
+    cfg = synth.config(2)
+    b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    print("case accuracy report config 2", flush=True)
+    q, k, v = synth.make_qkv_device(cfg)
+    q_cal, k_cal = synth.make_calibration(cfg)
+    s, inv, gate = hf.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
+    dims = hf.make_dims(b_n, hq, hkv, d, lq, lk)
+    res = hf.quantize_qkv(q, k, v, torch.from_numpy(s).cuda(), torch.from_numpy(inv).cuda(), dims=dims)
+    runs = {}
+    for name, mode in (("p_reordered", A.P_REORDERED), ("inconsistent", A.INCONSISTENT)):
+        print("  run", name, flush=True)
+        out, st = hf.attention_fwd(res, dims, True, mode, cfg["kv_tile"], tile_stats=True)
+        torch.cuda.synchronize()
+        runs[name] = (out, st.cpu().numpy())
+    st_c = runs["p_reordered"][1]
+    st_i = runs["inconsistent"][1]
+    assert np.array_equal(st_c, st_i), "tile sums must not depend on the normalizer"
+    eps, eps_report = _eps_stats(st_c)
+    assert np.all(np.isfinite(eps))
+    assert eps_report["median"] < 0, "P-hat flushes small probabilities: a net mass loss per tile"
+
+    # error against unquantized FP32 attention on sampled heads (all rows of each)
+    err = {"p_reordered": [], "inconsistent": []}
+    heads = [(0, 0), (2, 9), (5, 22), (7, 31)]
+    group = hq // hkv
+    for (b, h) in heads:
+        g = h // group
+        ref = A.reference_fp32(q[b, h].cpu().numpy(), k[b, g].cpu().numpy(), v[b, g].cpu().numpy(), True)
+        ref = ref.astype(np.float64)
+        for name in err:
+            got = runs[name][0][b, h].cpu().numpy().astype(np.float64)
+            diff = got - ref
+            err[name].append({
+                "head": [b, h],
+                "rel_rms": float(np.sqrt(np.mean(diff ** 2)) / np.sqrt(np.mean(ref ** 2))),
+                "max_abs": float(np.max(np.abs(diff))),
+                "cos": float(np.sum(got * ref) / np.sqrt(np.sum(got ** 2) * np.sum(ref ** 2))),
+                # per-row least-squares scale of got onto ref: Theorem 1's coherent factor
+                "row_scale_median": float(np.median(np.sum(got * ref, axis=1) / np.maximum(np.sum(ref * ref, axis=1), 1e-30))),
+            })
+    report = {"workload": cfg["name"], "epsilon_per_tile": eps_report,
+              "vs_fp32_attention": {k2: {
+                  "rel_rms_mean": float(np.mean([e["rel_rms"] for e in v2])),
+                  "max_abs": float(np.max([e["max_abs"] for e in v2])),
+                  "cos_min": float(np.min([e["cos"] for e in v2])),
+                  "row_scale_median": float(np.median([e["row_scale_median"] for e in v2])),
+                  "heads": v2} for k2, v2 in err.items()}}
+    print(json.dumps(report, indent=1), flush=True)
+    path = os.environ.get("HIFA4_REPORT")
+    if path:
+        with open(path, "w") as f:
+            json.dump(report, f, indent=1)
+    for name in err:
+        assert all(np.isfinite(e["rel_rms"]) for e in err[name])
