@@ -49,33 +49,22 @@ struct Cfg {
   static constexpr int kCB = D / 16;                      // 16-channel output blocks
   static constexpr int kKRow = D / 2;                     // bytes of one K-hat key row
   static constexpr int kNB = D / kBlock;                  // scale blocks per key
-  // byte offsets inside one LDS stage
-  static constexpr int kKC = 0;                                   // K-hat codes [128][D/2]
-  static constexpr int kVC = kKC + kTileKeys * kKRow;             // V-hat^T codes [D][64]
-  static constexpr int kKS = kVC + D * (kTileKeys / 2);           // K-hat scales [D/32][128]
+  // byte offsets inside one LDS stage; the codes are stored in MFMA-operand order, 1 KB per
+  // MFMA ([mfma][lane], 16 bytes per lane), so every operand read is a linear wave-wide read
+  static constexpr int kKC = 0;                                   // K-hat: 8 x KSTEPS MFMAs
+  static constexpr int kVC = kKC + 8 * kKSteps * 1024;            // V-hat^T: CB MFMAs
+  static constexpr int kKS = kVC + kCB * 1024;                    // K-hat scales [D/32][128]
   static constexpr int kVS = kKS + kTileKeys * kNB;               // V-hat scales [4][D]
   static constexpr int kStageBytes = kVS + 4 * D;
   // wave-wide loads that fill one stage: codes at 16 bytes per lane (1 KB per load), scales at
   // 4 bytes per lane (256 bytes per load)
-  static constexpr int kKCInstr = kTileKeys * kKRow / 1024;
-  static constexpr int kVCInstr = D * (kTileKeys / 2) / 1024;
+  static constexpr int kKCInstr = 8 * kKSteps;
+  static constexpr int kVCInstr = kCB;
   static constexpr int kKSInstr = kTileKeys * kNB / 256;
   static constexpr int kVSInstr = 4 * D / 256;
   static constexpr int kInstr = kKCInstr + kVCInstr + kKSInstr + kVSInstr;
   static constexpr int kMaxLoadsPerWave = (kInstr + kWaves - 1) / kWaves;
 };
-
-// XOR swizzles of the 16-byte chunks inside an LDS row.  One MFMA operand read touches, per
-// 16-lane group, keys 32b + 4t + a (b = col/4, a = col%4) of K-hat, or channels 16cb + col of
-// V-hat; the swizzle makes the 16-byte slots of any 8 consecutive lanes distinct modulo 128 bytes
-// and of any 16 lanes distinct modulo 256 bytes, so the read is conflict-free whether the LDS
-// serves it in 8-lane (32-bank) or 16-lane (64-bank) passes.  Both terms are fixed per lane.
-// Each is an involution: applied to a stored position it gives the chunk stored there.
-template <int D>
-__device__ __forceinline__ int kswz(int key, int chunk) {
-  return D >= 128 ? chunk ^ (((key >> 5) & 3) ^ (((key >> 1) & 1) << 1)) : chunk ^ ((key >> 5) & 1);
-}
-__device__ __forceinline__ int vswz(int ch, int chunk) { return chunk ^ (((ch >> 2) & 3) ^ (((ch >> 1) & 1) << 1)); }
 
 __device__ __forceinline__ float wave_sum16(float x) {  // sum over the 16 lanes sharing l / 16
   x += __shfl_xor(x, 1);
@@ -91,10 +80,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // scales), its byte offset inside the stage (the same for all lanes: the hardware writes lane i
 // at that offset + i * size) and this lane's byte offset inside the (batch, KV head) slice of
 // its section at key 0.  Positions are inverted here: a lane loads whatever HBM bytes belong at
-// its LDS position.  K-hat row R = 32a + 4t + b holds key 32a + 8b + t (the row MFMA t's lane
-// 4a + b reads, see score_row_key) and V-hat^T row R = 16cb + col holds channel CB col + cb (the
-// row PV MFMA cb's lane col reads), so each MFMA operand read is one fixed per-lane address plus
-// an immediate; the 16-byte chunks of both are XOR-swizzled (kswz, vswz).
+// its LDS position.  The code loads are exactly the operands of one MFMA: lane (g, col) of score
+// MFMA t fetches chunk g of key score_row_key(t, col); lane (g, col) of PV MFMA cb fetches the
+// 32-key block g of channel CB col + cb.  The scale loads copy the block-plane K-hat rows and the
+// V-hat block rows of the tile.
 struct LoadOp {
   int sec;
   int lds;
@@ -105,22 +94,19 @@ template <int D>
 __device__ __forceinline__ LoadOp load_op(int i, int lane, int lk32) {
   using C = Cfg<D>;
   LoadOp op;
+  const int g = lane >> 4, col = lane & 15;
   if (i < C::kKCInstr) {
-    const int pos = i * 1024 + 16 * lane;
-    const int r = pos / C::kKRow, p = (pos % C::kKRow) / 16;
-    const int c = D >= 128 ? ((p & ~3) | kswz<D>(r, p & 3)) : kswz<D>(r, p);
-    const int key = 32 * (r >> 5) + 8 * (r & 3) + ((r >> 2) & 7);
+    const int t = i / C::kKSteps, st = i % C::kKSteps;
+    // d = 64 has two chunks per key: lanes g >= 2 fetch a duplicate that no MFMA reads
+    const int chunk = D >= 128 ? 4 * st + g : (g & 1);
     op.sec = 0;
     op.lds = C::kKC + i * 1024;
-    op.voff = key * C::kKRow + 16 * c;
+    op.voff = score_row_key(t, col) * C::kKRow + 16 * chunk;
   } else if (i < C::kKCInstr + C::kVCInstr) {
-    const int q = i - C::kKCInstr;
-    const int pos = q * 1024 + 16 * lane;
-    const int r = pos / 64, part = vswz(r, (pos % 64) / 16);
-    const int ch = C::kCB * (r % 16) + r / 16;
+    const int cb = i - C::kKCInstr;
     op.sec = 1;
-    op.lds = C::kVC + q * 1024;
-    op.voff = (part * D + ch) * 16;  // block-major V-hat: (32-key block, channel) cells
+    op.lds = C::kVC + cb * 1024;
+    op.voff = (g * D + C::kCB * col + cb) * 16;  // block-major V-hat: (32-key block, channel) cells
   } else if (i < C::kKCInstr + C::kVCInstr + C::kKSInstr) {
     const int q = i - C::kKCInstr - C::kVCInstr;
     const int pos = q * 256 + 4 * lane;  // [block][key] rows of 128 bytes
@@ -301,9 +287,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
   const float C = a.c_log2;
 
   // per-lane LDS offsets of this lane's MFMA operands (see the reads in the tile loop)
-  const int k_lane_off = Cf::kKC + (32 * (col >> 2) + (col & 3)) * (D / 2) + 16 * kswz<D>(32 * (col >> 2) + (col & 3), g);
+  const int k_lane_off = Cf::kKC + 16 * lane;
   const int ks_lane_off = Cf::kKS + g * kTileKeys + 32 * (col >> 2) + 8 * (col & 3);
-  const int v_lane_off = Cf::kVC + col * 64 + 16 * vswz(col, g);
+  const int v_lane_off = Cf::kVC + 16 * lane;
   const int vs_lane_off = Cf::kVS + g * D + CB * col;
 
   // prologue: tiles 0 .. kStages-2 in flight, wait for tile 0
@@ -321,9 +307,8 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
     if (ahead < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
 
     if (wave_live && !(CAUSAL && k0 > wave_last + shift)) {
-      // ---- S^T = K-hat Q-hat^T: MFMA t reads key kr = 32 (col/4) + 4t + (col%4); the per-lane
-      // part is a fixed base, t and the contraction step are immediate offsets (the swizzle term
-      // kr/32 = col/4 does not depend on t).  Lane holds keys k0 + 32 g + (4 t + i).
+      // ---- S^T = K-hat Q-hat^T: MFMA t takes key score_row_key(t, r) as row r; its operands sit
+      // in LDS in lane order.  Lane (g, col) then holds keys 32 g + 8 i + t in s[4 t + i].
       const uint8_t* kbase = T + k_lane_off;
       // the lane's 8 K-hat scale bytes of each contraction step (byte t serves MFMA t)
       uint2 ksw[KSTEPS];
@@ -339,7 +324,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
 #pragma unroll
         for (int st = 0; st < KSTEPS; st++) {
           uint4 ka = make_uint4(0u, 0u, 0u, 0u);
-          if (D >= 128 || g < 2) ka = *reinterpret_cast<const uint4*>(kbase + 4 * t * (D / 2) + 64 * st);
+          if (D >= 128 || g < 2) ka = *reinterpret_cast<const uint4*>(kbase + 1024 * (KSTEPS * t + st));
           const uint32_t kw = t < 4 ? ksw[st].x : ksw[st].y;
           switch (t & 3) {
             case 0: acc = mfma_fp4_sel<0, 0>(ka, kw, qreg[st], qsc[st], acc); break;
@@ -397,8 +382,8 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
           }
         }
       }
-      // ---- O^T += V-hat^T P-hat^T per 16-channel block (channel 16 cb + col; the swizzle term
-      // (ch/4)%4 = col/4); FP16 state update
+      // ---- O^T += V-hat^T P-hat^T per channel block (PV MFMA cb takes channel CB r + cb as row
+      // r; operands in lane order); FP16 state update
       const uint8_t* vbase = T + v_lane_off;
       // the lane's CB V-hat scale bytes (byte cb serves channel block cb)
       uint32_t vsw[CB / 4];
@@ -417,7 +402,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs
       }
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
-        const uint4 va = *reinterpret_cast<const uint4*>(vbase + 16 * 64 * cb);
+        const uint4 va = *reinterpret_cast<const uint4*>(vbase + 1024 * cb);
         const uint32_t vw = vsw[cb / 4];
         v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
         switch (cb & 3) {
