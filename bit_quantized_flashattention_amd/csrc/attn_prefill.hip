@@ -36,6 +36,9 @@ constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wav
 #ifndef PREFILL_WAVES
 #define PREFILL_WAVES 8  // waves per work-group: 8 x 16 query rows
 #endif
+#ifndef PREFILL_MIN_WAVES
+#define PREFILL_MIN_WAVES 6  // waves per SIMD the register allocation must allow: 3 work-groups per CU
+#endif
 #ifndef PREFILL_STAGES
 #define PREFILL_STAGES 2
 #endif
@@ -201,7 +204,7 @@ __device__ __forceinline__ void wait_vmem_n(int n) {
 }
 
 template <int D, bool CAUSAL, int MODE, bool STATS>
-__global__ __launch_bounds__(Cfg<D>::kThreads) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, PREFILL_MIN_WAVES) void attn_prefill_kernel(AttnArgs a) {
   using Cf = Cfg<D>;
   constexpr int W = Cf::kWaves;
   constexpr int KSTEPS = Cf::kKSteps;
