@@ -37,7 +37,7 @@ constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wav
 #define PREFILL_WAVES 8  // waves per work-group: 8 x 16 query rows
 #endif
 #ifndef PREFILL_MIN_WAVES
-#define PREFILL_MIN_WAVES 6  // waves per SIMD the register allocation must allow: 3 work-groups per CU
+#define PREFILL_MIN_WAVES 6  // waves per SIMD the P-Reordered kernels' registers must allow (3 work-groups per CU)
 #endif
 #ifndef PREFILL_STAGES
 #define PREFILL_STAGES 2
@@ -204,7 +204,7 @@ __device__ __forceinline__ void wait_vmem_n(int n) {
 }
 
 template <int D, bool CAUSAL, int MODE, bool STATS>
-__global__ __launch_bounds__(Cfg<D>::kThreads, PREFILL_MIN_WAVES) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_MIN_WAVES : 4) void attn_prefill_kernel(AttnArgs a) {
   using Cf = Cfg<D>;
   constexpr int W = Cf::kWaves;
   constexpr int KSTEPS = Cf::kKSteps;
@@ -320,24 +320,35 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, PREFILL_MIN_WAVES) void attn_pref
         ksw[st] = *reinterpret_cast<const uint2*>(T + ks_lane_off + 4 * kTileKeys * st);
         if (D < 128 && g >= 2) ksw[st] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
       }
+      // operands read two MFMAs ahead into a double buffer, so LDS latency hides behind the
+      // matrix pipe instead of stalling each MFMA
+      constexpr int NK = 8 * KSTEPS;
+      auto kop = [&](int j) -> uint4 {
+        if (D < 128 && g >= 2) return make_uint4(0u, 0u, 0u, 0u);
+        return *reinterpret_cast<const uint4*>(kbase + 1024 * j);
+      };
+      uint4 ka[2];
+      ka[0] = kop(0);
+      ka[1] = kop(1);
       float s[32];
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int t = 0; t < 8; t++) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < KSTEPS; st++) {
-          uint4 ka = make_uint4(0u, 0u, 0u, 0u);
-          if (D >= 128 || g < 2) ka = *reinterpret_cast<const uint4*>(kbase + 1024 * (KSTEPS * t + st));
-          const uint32_t kw = t < 4 ? ksw[st].x : ksw[st].y;
-          switch (t & 3) {
-            case 0: acc = mfma_fp4_sel<0, 0>(ka, kw, qreg[st], qsc[st], acc); break;
-            case 1: acc = mfma_fp4_sel<1, 0>(ka, kw, qreg[st], qsc[st], acc); break;
-            case 2: acc = mfma_fp4_sel<2, 0>(ka, kw, qreg[st], qsc[st], acc); break;
-            default: acc = mfma_fp4_sel<3, 0>(ka, kw, qreg[st], qsc[st], acc); break;
-          }
+      for (int j = 0; j < NK; j++) {
+        const int t = j / KSTEPS, st = j % KSTEPS;
+        if (st == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t kw = t < 4 ? ksw[st].x : ksw[st].y;
+        switch (t & 3) {
+          case 0: acc = mfma_fp4_sel<0, 0>(ka[j & 1], kw, qreg[st], qsc[st], acc); break;
+          case 1: acc = mfma_fp4_sel<1, 0>(ka[j & 1], kw, qreg[st], qsc[st], acc); break;
+          case 2: acc = mfma_fp4_sel<2, 0>(ka[j & 1], kw, qreg[st], qsc[st], acc); break;
+          default: acc = mfma_fp4_sel<3, 0>(ka[j & 1], kw, qreg[st], qsc[st], acc); break;
         }
+        if (j + 2 < NK) ka[j & 1] = kop(j + 2);
+        if (st == KSTEPS - 1) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) s[4 * t + i] = acc[i];
+          for (int i = 0; i < 4; i++) s[4 * t + i] = acc[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       const int q = q0 + col;
       const bool full = bc == kTileKeys && k0 + kTileKeys <= lk && q0 + 15 < lq &&
@@ -403,19 +414,27 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, PREFILL_MIN_WAVES) void attn_pref
         vsw[2] = w.z;
         vsw[3] = w.w;
       }
+      // V-hat operands two MFMAs ahead; the state update of block cb - 1 follows MFMA cb, so the
+      // matrix result latency is covered by the next MFMA
+      uint4 va[2];
+      va[0] = *reinterpret_cast<const uint4*>(vbase);
+      va[1] = *reinterpret_cast<const uint4*>(vbase + 1024);
+      v4f pv[2];
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
-        const uint4 va = *reinterpret_cast<const uint4*>(vbase + 1024 * cb);
         const uint32_t vw = vsw[cb / 4];
-        v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
+        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
         switch (cb & 3) {
-          case 0: pv = mfma_fp4_sel<0, 0>(va, vw, ph, psc, pv); break;
-          case 1: pv = mfma_fp4_sel<1, 0>(va, vw, ph, psc, pv); break;
-          case 2: pv = mfma_fp4_sel<2, 0>(va, vw, ph, psc, pv); break;
-          default: pv = mfma_fp4_sel<3, 0>(va, vw, ph, psc, pv); break;
+          case 0: pv[cb & 1] = mfma_fp4_sel<0, 0>(va[cb & 1], vw, ph, psc, z); break;
+          case 1: pv[cb & 1] = mfma_fp4_sel<1, 0>(va[cb & 1], vw, ph, psc, z); break;
+          case 2: pv[cb & 1] = mfma_fp4_sel<2, 0>(va[cb & 1], vw, ph, psc, z); break;
+          default: pv[cb & 1] = mfma_fp4_sel<3, 0>(va[cb & 1], vw, ph, psc, z); break;
         }
-        state_update(o[cb], rs.alpha, pv);
+        if (cb + 2 < CB) va[cb & 1] = *reinterpret_cast<const uint4*>(vbase + 1024 * (cb + 2));
+        if (cb >= 1) state_update(o[cb - 1], rs.alpha, pv[(cb - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      state_update(o[CB - 1], rs.alpha, pv[(CB - 1) & 1]);
       l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
       m = rs.m_new;
     }
