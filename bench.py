@@ -2,17 +2,20 @@
 """Benchmark of the 4-bit (HiFA4-style) attention forward on one MI355X.
 
 A step is one pass of the hot path over one batch of resident synthetic input:
-the Smooth-QK rescale + 4-bit quantization of Q, K, V (HBM-bound kernel) followed
-by the fused 4-bit attention forward.  The default workload is the batched causal
-prefill (B=8, L=4096, Hq=32/Hkv=8, d=128, P-Reordered normalizer, 128-key tiles).
-The JSON line also carries the memory-bound split-KV decode (B=64, Lk=32768,
-pre-quantized cache; a step quantizes the query token and runs split + merge).
+the Smooth-QK rescale + 4-bit quantization of K and V (HBM-bound kernels) followed
+by the fused 4-bit attention forward, which rescales and quantizes its own query
+rows on the way in (hifa4_attention_fwd_q16).  The default workload is the batched
+causal prefill (B=8, L=4096, Hq=32/Hkv=8, d=128, P-Reordered normalizer, 128-key
+tiles).  The JSON line also carries the memory-bound split-KV decode (B=64,
+Lk=32768, pre-quantized cache; a step runs split, with the query token quantized
+in-kernel, and merge).  The default warm-up (50 steps, about 40 ms) lets the GPU
+clocks settle before the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
 
 Rates: algorithmic FLOPs are 4 * d per visible (query, key) pair (L(L+1)/2 pairs
-per head when causal); decode bytes are the K-hat/V-hat codes and scales, Q-hat
-and the FP16 output.  Kernel durations come from HIP events recorded on the
+per head when causal); decode bytes are the K-hat/V-hat codes and scales, the FP16
+query, the Smooth-QK scales and the FP16 output.  Kernel durations come from HIP events recorded on the
 stream the kernels run on.  Peaks: MI355X dense FP4 MFMA 10.1 PFLOP/s, HBM3E
 8 TB/s (AMD's published figures).
 """
@@ -36,8 +39,8 @@ KERNEL_SOURCES = ["attn_prefill.hip", "attn_decode.hip", "device_common.h", "qua
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
@@ -114,10 +117,11 @@ def bench_prefill(args, cfg_id):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        hf.quantize_qkv(q, k, v, sd, invd, dims=dims, out=qkv)
+        # K-hat, V-hat from the quantizer; Q is rescaled and quantized inside the attention kernel
+        hf.quantize_qkv(None, k, v, sd, invd, dims=dims, out=qkv)
         if ev is not None:
             ev[0].record(stream)
-        hf.attention_fwd(qkv, dims, cfg["causal"], hf.P_REORDERED, cfg["kv_tile"], out=out)
+        hf.attention_fwd(qkv, dims, cfg["causal"], hf.P_REORDERED, cfg["kv_tile"], out=out, q16=(q, sd))
         if ev is not None:
             ev[1].record(stream)
 
@@ -161,10 +165,10 @@ def bench_decode(args):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        hf.quantize_qkv(q, None, None, sd, invd, dims=dims, out=qkv)
         if ev is not None:
             ev[0].record(stream)
-        hf.attention_fwd(qkv, dims, True, hf.P_REORDERED, cfg["kv_tile"], 0, out=out, workspace=ws)
+        # the FP16 query is rescaled and quantized inside the split kernel
+        hf.attention_fwd(qkv, dims, True, hf.P_REORDERED, cfg["kv_tile"], 0, out=out, workspace=ws, q16=(q, sd))
         if ev is not None:
             ev[1].record(stream)
 
@@ -183,7 +187,7 @@ def bench_decode(args):
     lk32 = -(-lk // 32) * 32
     kv_bytes = 2 * b * hkv * (lk * d // 2 + lk * d // 32)  # K-hat and V-hat codes + scales
     assert kv_bytes == b * hkv * (lk * (d // 2 + d // 32) + d * (lk32 // 2 + lk32 // 32))
-    q_bytes = b * hq * (d // 2 + d // 32)
+    q_bytes = b * hq * d * 2 + hkv * d * 4  # FP16 query and the Smooth-QK scales
     out_bytes = b * hq * d * 2
     total = kv_bytes + q_bytes + out_bytes
     res = {
@@ -239,8 +243,7 @@ def cpu_baseline(args, pre):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path (see DESIGN.md); use --gpus 1",
-              file=sys.stderr)
+        print("bench.py runs on one GPU; there is no multi-GPU path: use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
@@ -263,7 +266,7 @@ def main():
         "dtype": "fp4",
         "data": "synthetic",
         "config": {
-            "workload": "%s: causal=%s B%d Hq%d/Hkv%d d%d L%d, kv_tile %d, quantize + attention per step"
+            "workload": "%s: causal=%s B%d Hq%d/Hkv%d d%d L%d, kv_tile %d, per step: K/V quantize + attention with Q quantized in-kernel"
                         % (cfg["name"], cfg["causal"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lq"],
                            cfg["kv_tile"]),
             "global_batch": cfg["B"], "seq_len": cfg["Lq"], "heads_q": cfg["Hq"], "heads_kv": cfg["Hkv"],

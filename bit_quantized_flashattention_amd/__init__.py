@@ -56,6 +56,9 @@ def lib():
         L.hifa4_attention_fwd.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 8 + \
             [ctypes.c_size_t, _vp, _vp]
         L.hifa4_attention_fwd.restype = ctypes.c_int
+        L.hifa4_attention_fwd_q16.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 8 + \
+            [ctypes.c_size_t, _vp, _vp]
+        L.hifa4_attention_fwd_q16.restype = ctypes.c_int
         L.hifa4_status_string.argtypes = [ctypes.c_int]
         L.hifa4_status_string.restype = ctypes.c_char_p
         L.hifa4_last_error.argtypes = []
@@ -171,15 +174,19 @@ def stats_shape(dims, kv_tile):
 
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
-                  out=None, workspace=None, tile_stats=None, stream=None):
+                  out=None, workspace=None, tile_stats=None, stream=None, q16=None):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
+
+    ``q16=(q, s)``: take FP16 Q and the Smooth-QK scales (device tensor or None) instead of
+    qkv's Q-hat and quantize Q inside the kernel (hifa4_attention_fwd_q16); qkv then needs only
+    the K-hat and V-hat entries.
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
     """
     import torch
     opts = make_opts(causal, normalizer, kv_tile, num_splits)
-    dev = qkv["q_codes"].device
+    dev = qkv["k_codes"].device
     if out is None:
         out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16, device=dev)
     need = attention_workspace_bytes(dims, opts)
@@ -190,8 +197,15 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
         stats = torch.empty(stats_shape(dims, kv_tile), dtype=torch.float32, device=dev)
     elif tile_stats is not None:
         stats = tile_stats
-    _check(lib().hifa4_attention_fwd(
-        ctypes.byref(dims), ctypes.byref(opts), _ptr(qkv["q_codes"]), _ptr(qkv["q_scales"]), _ptr(qkv["k_codes"]),
-        _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
-        workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
+    if q16 is None:
+        _check(lib().hifa4_attention_fwd(
+            ctypes.byref(dims), ctypes.byref(opts), _ptr(qkv["q_codes"]), _ptr(qkv["q_scales"]), _ptr(qkv["k_codes"]),
+            _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
+    else:
+        q, s = q16
+        _check(lib().hifa4_attention_fwd_q16(
+            ctypes.byref(dims), ctypes.byref(opts), _ptr(q), _ptr(s), _ptr(qkv["k_codes"]),
+            _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
     return (out, stats) if tile_stats is not None else out

@@ -91,13 +91,27 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   // Q-hat^T operand: column = query head, K-chunk g
   uint4 qreg[KSTEPS];
   uint32_t qsc[KSTEPS];
-  const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (D / 2);
-  const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (D / kBlock);
+  if (a.q_fp16 != nullptr) {
+    // FP16 Q: this lane quantizes its own 32-element block (4 st + g) of query head h
+    const uint16_t* qx = a.q_fp16 + ((int64_t)b * a.heads_q + h) * D;
 #pragma unroll
-  for (int st = 0; st < KSTEPS; st++) {
-    const bool ok = live_col && (D >= 128 || g < 2);
-    qreg[st] = ok ? *reinterpret_cast<const uint4*>(qc + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-    qsc[st] = ok ? qs[4 * st + g] : 127u;
+    for (int st = 0; st < KSTEPS; st++) {
+      qreg[st] = make_uint4(0u, 0u, 0u, 0u);
+      qsc[st] = 127u;
+      if (live_col && (D >= 128 || g < 2)) {
+        const int c0 = 128 * st + 32 * g;
+        qsc[st] = quantize_block32(qx + c0, a.q_smooth ? a.q_smooth + (int64_t)kvh * D + c0 : nullptr, &qreg[st]);
+      }
+    }
+  } else {
+    const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (D / 2);
+    const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (D / kBlock);
+#pragma unroll
+    for (int st = 0; st < KSTEPS; st++) {
+      const bool ok = live_col && (D >= 128 || g < 2);
+      qreg[st] = ok ? *reinterpret_cast<const uint4*>(qc + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+      qsc[st] = ok ? qs[4 * st + g] : 127u;
+    }
   }
 
   const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);

@@ -203,6 +203,11 @@ __device__ __forceinline__ void wait_vmem_n(int n) {
   }
 }
 
+// Smooth-QK scales of channels c0 .. c0+31 of KV head kvh, or nullptr for no rescale.
+__device__ __forceinline__ const float* q_smooth_blk(const AttnArgs& a, int kvh, int d, int c0) {
+  return a.q_smooth != nullptr ? a.q_smooth + (int64_t)kvh * d + c0 : nullptr;
+}
+
 template <int D, bool CAUSAL, int MODE, bool STATS>
 __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_MIN_WAVES : 4) void attn_prefill_kernel(AttnArgs a) {
   using Cf = Cfg<D>;
@@ -236,20 +241,35 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   // ---- Q-hat^T operand (B operand of the score MFMA), kept in registers
   uint4 qreg[KSTEPS];
   uint32_t qsc[KSTEPS];
+  // FP16 Q (fused quantization): this lane's own 32-element block (4s + g) of query row q0 + col
+  // is loaded here and quantized once the first K/V tile is in flight, so the two latencies overlap
+  const bool fused_q = a.q_fp16 != nullptr;
+  const bool q_has = q0 + col < lq && (D >= 128 || g < 2);
+  Block32In qin[KSTEPS];
   {
-    const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / 2);
-    const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / kBlock);
     const int q = q0 + col;
+    if (fused_q) {
+      if (q_has) {
+        const uint16_t* qx = a.q_fp16 + (((int64_t)b * a.heads_q + h) * lq + q) * D;
+        // the channel scales are loaded with the values where registers allow (one K-step)
 #pragma unroll
-    for (int s = 0; s < KSTEPS; s++) {
-      const bool has = q < lq && (D >= 128 || g < 2);
-      qreg[s] = has ? *reinterpret_cast<const uint4*>(qc + (int64_t)q * (D / 2) + 64 * s + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-      qsc[s] = has ? qs[(int64_t)q * (D / kBlock) + 4 * s + g] : 127u;
+        for (int s = 0; s < KSTEPS; s++)
+          load_block32(qx + 128 * s + 32 * g, KSTEPS == 1 ? q_smooth_blk(a, kvh, D, 128 * s + 32 * g) : nullptr, qin[s]);
+      }
+    } else {
+      const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / 2);
+      const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / kBlock);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; s++) {
+        const bool has = q < lq && (D >= 128 || g < 2);
+        qreg[s] = has ? *reinterpret_cast<const uint4*>(qc + (int64_t)q * (D / 2) + 64 * s + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+        qsc[s] = has ? qs[(int64_t)q * (D / kBlock) + 4 * s + g] : 127u;
+      }
     }
   }
 
   // the Q-hat loads complete here, so no wait for them lands inside the tile loop
-  wait_vmem<0>();
+  if (!fused_q) wait_vmem<0>();
 
   // ---- FP16 state; m is an integer-valued float
   h2 o[CB][2];
@@ -299,6 +319,18 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
 #pragma unroll
   for (int p = 0; p < kStages - 1; p++)
     if (p < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
+  if (fused_q) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; s++) {
+      qreg[s] = make_uint4(0u, 0u, 0u, 0u);
+      qsc[s] = 127u;
+      if (q_has) {
+        if (KSTEPS > 1) load_block32(nullptr, q_smooth_blk(a, kvh, D, 128 * s + 32 * g), qin[s]);
+        qsc[s] = quantize_loaded32(qin[s], a.q_smooth != nullptr, &qreg[s]);
+      }
+    }
+  }
   if (kStages > 2 && n_tiles > 1) wait_vmem_n<Cf::kMaxLoadsPerWave>(n_loads);
   else wait_vmem<0>();
   __syncthreads();

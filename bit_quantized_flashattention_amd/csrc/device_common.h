@@ -49,6 +49,70 @@ __device__ __forceinline__ uint32_t pack8_fp4(const float* v, float scale) {
   return w;
 }
 
+// Inputs of one 32-element block quantization: 32 FP16 values and their 32 FP32 channel scales.
+struct Block32In {
+  uint4 x[4];
+  float4 s[8];
+};
+
+// Issues the loads of one block: x points at 32 FP16 values (16-byte aligned), s at their FP32
+// channel scales; either may be nullptr to leave that part of in untouched.
+__device__ __forceinline__ void load_block32(const uint16_t* x, const float* s, Block32In& in) {
+  if (x != nullptr) {
+    const uint4* src = reinterpret_cast<const uint4*>(x);
+#pragma unroll
+    for (int i = 0; i < 4; i++) in.x[i] = src[i];
+  }
+  if (s != nullptr) {
+    const float4* sc = reinterpret_cast<const float4*>(s);
+#pragma unroll
+    for (int i = 0; i < 8; i++) in.s[i] = sc[i];
+  }
+}
+
+// Smooth-QK rescale and 4-bit quantization of one loaded block (scaled: apply in.s).  Each value
+// becomes fp32(x * s) (one rounding; contraction is off), the block exponent comes from the
+// largest magnitude, and the codes are RNE onto E2M1 relative to 2^e.  Returns the E8M0 scale
+// byte (e + 127); the 16 code bytes go to *codes (element 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool scaled, uint4* codes) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w[4] = {in.x[i].x, in.x[i].y, in.x[i].z, in.x[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[i * 8 + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFF));
+      v[i * 8 + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+    }
+  }
+  if (scaled) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[4 * i + 0] = v[4 * i + 0] * in.s[i].x;
+      v[4 * i + 1] = v[4 * i + 1] * in.s[i].y;
+      v[4 * i + 2] = v[4 * i + 2] * in.s[i].z;
+      v[4 * i + 3] = v[4 * i + 3] * in.s[i].w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+  const float scale = e8m0_as_float(e);
+  codes->x = pack8_fp4(v + 0, scale);
+  codes->y = pack8_fp4(v + 8, scale);
+  codes->z = pack8_fp4(v + 16, scale);
+  codes->w = pack8_fp4(v + 24, scale);
+  return (uint32_t)(e + 127);
+}
+
+// Both steps for one block (see load_block32 and quantize_loaded32).
+__device__ __forceinline__ uint32_t quantize_block32(const uint16_t* x, const float* s, uint4* codes) {
+  Block32In in;
+  load_block32(x, s, in);
+  return quantize_loaded32(in, s != nullptr, codes);
+}
+
 // log2(6) rounded to the nearest FP32 (0x40257007): 6 is the largest E2M1 magnitude.
 constexpr float kLog2Six = 0x1.4ae00ep+1f;
 

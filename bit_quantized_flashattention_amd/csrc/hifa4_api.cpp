@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -100,6 +101,13 @@ int32_t resolve_splits(const hifa4_dims* d, const hifa4_attn_opts* o) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// true when every non-NULL pointer of the list is 16-byte aligned
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & 15) != 0) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +120,7 @@ const char* hifa4_status_string(hifa4_status status) {
     case HIFA4_ERR_UNSUPPORTED: return "unsupported configuration";
     case HIFA4_ERR_WORKSPACE: return "workspace missing or too small";
     case HIFA4_ERR_HIP: return "HIP runtime error";
+    case HIFA4_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
   }
   return "unknown status";
 }
@@ -175,6 +184,8 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
   if (q && (!q_codes || !q_scales)) return fail(HIFA4_ERR_NULL, "quantize: q outputs are NULL");
   if (k && (!k_codes || !k_scales)) return fail(HIFA4_ERR_NULL, "quantize: k outputs are NULL");
   if (v && (!v_codes || !v_scales)) return fail(HIFA4_ERR_NULL, "quantize: v outputs are NULL");
+  if (!aligned16({q, k, v, s, inv_s, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales}))
+    return fail(HIFA4_ERR_ALIGNMENT, "quantize: device pointers must be 16-byte aligned");
   hipStream_t stream = (hipStream_t)hip_stream;
   const int group = dims->heads_q / dims->heads_kv;
   if (q) {
@@ -212,26 +223,14 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
   return align256((size_t)parts * dims->head_dim * 2) + align256((size_t)parts * 2 * 2);
 }
 
-hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* opts,
-                                 const void* q_codes, const void* q_scales, const void* k_codes,
-                                 const void* k_scales, const void* v_codes, const void* v_scales,
-                                 void* out, void* workspace, size_t workspace_bytes,
-                                 float* tile_stats, void* hip_stream) {
-  hifa4_status st = check_dims(dims);
-  if (st != HIFA4_OK) return st;
-  st = check_opts(dims, opts);
-  if (st != HIFA4_OK) return st;
-  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out)
-    return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
-  hifa4::AttnArgs a{};
-  a.q_codes = (const uint8_t*)q_codes;
-  a.q_scales = (const uint8_t*)q_scales;
-  a.k_codes = (const uint8_t*)k_codes;
-  a.k_scales = (const uint8_t*)k_scales;
-  a.v_codes = (const uint8_t*)v_codes;
-  a.v_scales = (const uint8_t*)v_scales;
-  a.out = (uint16_t*)out;
-  a.stats = tile_stats;
+}  // extern "C"
+
+namespace {
+
+// Shared tail of both attention entry points: a holds the tensor pointers; fills the sizes and
+// launches the prefill or split-KV decode kernel.
+hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const hifa4_attn_opts* opts,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
   a.batch = dims->batch;
   a.heads_q = dims->heads_q;
   a.heads_kv = dims->heads_kv;
@@ -247,7 +246,7 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
   hipStream_t stream = (hipStream_t)hip_stream;
   hipError_t e;
   if (dims->len_q == 1) {
-    if (tile_stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
+    if (a.stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
     const size_t need = hifa4_attention_workspace_bytes(dims, opts);
     if (workspace == nullptr || workspace_bytes < need)
       return fail(HIFA4_ERR_WORKSPACE, "attention: decode needs " + std::to_string(need) + " workspace bytes");
@@ -264,6 +263,59 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
   }
   if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* opts,
+                                 const void* q_codes, const void* q_scales, const void* k_codes,
+                                 const void* k_scales, const void* v_codes, const void* v_scales,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 float* tile_stats, void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  st = check_opts(dims, opts);
+  if (st != HIFA4_OK) return st;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+    return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
+  if (!aligned16({q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, out, workspace, tile_stats}))
+    return fail(HIFA4_ERR_ALIGNMENT, "attention: device pointers must be 16-byte aligned");
+  hifa4::AttnArgs a{};
+  a.q_codes = (const uint8_t*)q_codes;
+  a.q_scales = (const uint8_t*)q_scales;
+  a.k_codes = (const uint8_t*)k_codes;
+  a.k_scales = (const uint8_t*)k_scales;
+  a.v_codes = (const uint8_t*)v_codes;
+  a.v_scales = (const uint8_t*)v_scales;
+  a.out = (uint16_t*)out;
+  a.stats = tile_stats;
+  return attention_launch(a, dims, opts, workspace, workspace_bytes, hip_stream);
+}
+
+hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
+                                     const float* s, const void* k_codes, const void* k_scales,
+                                     const void* v_codes, const void* v_scales, void* out, void* workspace,
+                                     size_t workspace_bytes, float* tile_stats, void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  st = check_opts(dims, opts);
+  if (st != HIFA4_OK) return st;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+    return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
+  if (!aligned16({q, s, k_codes, k_scales, v_codes, v_scales, out, workspace, tile_stats}))
+    return fail(HIFA4_ERR_ALIGNMENT, "attention: device pointers must be 16-byte aligned");
+  hifa4::AttnArgs a{};
+  a.q_fp16 = (const uint16_t*)q;
+  a.q_smooth = s;
+  a.k_codes = (const uint8_t*)k_codes;
+  a.k_scales = (const uint8_t*)k_scales;
+  a.v_codes = (const uint8_t*)v_codes;
+  a.v_scales = (const uint8_t*)v_scales;
+  a.out = (uint16_t*)out;
+  a.stats = tile_stats;
+  return attention_launch(a, dims, opts, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -31,8 +31,10 @@ struct QuantVtArgs {
 };
 
 struct AttnArgs {
-  const uint8_t* q_codes;
+  const uint8_t* q_codes;   // Q-hat, or nullptr when q_fp16 is given
   const uint8_t* q_scales;
+  const uint16_t* q_fp16;   // FP16 Q [B, Hq, Lq, d] quantized in the kernel prologue, or nullptr
+  const float* q_smooth;    // Smooth-QK scales [Hkv, d] applied to q_fp16, or nullptr
   const uint8_t* k_codes;
   const uint8_t* k_scales;
   const uint8_t* v_codes;

@@ -32,46 +32,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   } else {
     scale_dst = a.scales + row * NB + blk;
   }
-  const uint4* src = reinterpret_cast<const uint4*>(a.x + row * D + blk * kBlock);
-  uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) raw[i] = src[i];
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFF));
-      const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
-      v[i * 8 + 2 * j] = (float)lo;
-      v[i * 8 + 2 * j + 1] = (float)hi;
-    }
-  }
+  const float* sc = nullptr;
   if (a.scale != nullptr) {
     const int h = (int)((row / a.len) % a.heads);
-    const float4* sc = reinterpret_cast<const float4*>(a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock);
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const float4 s4 = sc[i];
-      v[4 * i + 0] = v[4 * i + 0] * s4.x;  // one FP32 rounding (contraction is off)
-      v[4 * i + 1] = v[4 * i + 1] * s4.y;
-      v[4 * i + 2] = v[4 * i + 2] * s4.z;
-      v[4 * i + 3] = v[4 * i + 3] * s4.w;
-    }
+    sc = a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock;
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-  const int e = mx_exponent(amax);
-  const float sc = e8m0_as_float(e);
   uint4 out;
-  out.x = pack8_fp4(v + 0, sc);
-  out.y = pack8_fp4(v + 8, sc);
-  out.z = pack8_fp4(v + 16, sc);
-  out.w = pack8_fp4(v + 24, sc);
+  const uint32_t e8 = quantize_block32(a.x + row * D + blk * kBlock, sc, &out);
   *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + blk * 16) = out;
-  *scale_dst = (uint8_t)(e + 127);
+  *scale_dst = (uint8_t)e8;
 }
 
 // V: blocks run along tokens, so a work-group stages 128 tokens x d channels in LDS and each

@@ -27,7 +27,7 @@
  *   s, inv_s FP32 [Hkv, d]                   (query head h uses KV head h / (Hq/Hkv))
  *
  * Conventions: the caller owns every buffer; device pointers come from hipMalloc (or PyTorch's
- * allocator); device calls are asynchronous on the given HIP stream (NULL = default stream) and
+ * allocator) and must be 16-byte aligned (the kernels move 16-byte vectors); device calls are asynchronous on the given HIP stream (NULL = default stream) and
  * never synchronize; no C++ exception crosses the ABI; a failed call launches nothing, returns a
  * status and leaves a description in hifa4_last_error() (thread-local).  The only global state
  * is that thread-local string, so calls from several threads are safe.
@@ -52,7 +52,8 @@ typedef enum {
   HIFA4_ERR_SHAPE = 2,       /* inconsistent or out-of-range dimensions */
   HIFA4_ERR_UNSUPPORTED = 3, /* valid request this library does not implement */
   HIFA4_ERR_WORKSPACE = 4,   /* workspace missing or too small */
-  HIFA4_ERR_HIP = 5          /* the HIP runtime reported an error (launch, device) */
+  HIFA4_ERR_HIP = 5,         /* the HIP runtime reported an error (launch, device) */
+  HIFA4_ERR_ALIGNMENT = 6    /* a device pointer is not 16-byte aligned */
 } hifa4_status;
 
 typedef struct {
@@ -100,7 +101,7 @@ hifa4_status hifa4_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64
  * Any of q, k, v may be NULL to skip that tensor (its outputs are then not touched); s and inv_s
  * may be NULL for no rescale (both or neither).  Outputs use the layouts above.
  * Errors: HIFA4_ERR_NULL (an output of a present input is NULL), HIFA4_ERR_SHAPE,
- * HIFA4_ERR_UNSUPPORTED (d), HIFA4_ERR_HIP.
+ * HIFA4_ERR_UNSUPPORTED (d), HIFA4_ERR_ALIGNMENT, HIFA4_ERR_HIP.
  */
 hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const void* k,
                                 const void* v, const float* s, const float* inv_s,
@@ -129,13 +130,27 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * query rows and key tile, (sum of P-hat, sum of P-tilde) over visible entries (zeros for tiles
  * a row block never visits); prefill only.
  * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE, HIFA4_ERR_UNSUPPORTED, HIFA4_ERR_WORKSPACE,
- * HIFA4_ERR_HIP.
+ * HIFA4_ERR_ALIGNMENT, HIFA4_ERR_HIP.
  */
 hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* opts,
                                  const void* q_codes, const void* q_scales, const void* k_codes,
                                  const void* k_scales, const void* v_codes, const void* v_scales,
                                  void* out, void* workspace, size_t workspace_bytes,
                                  float* tile_stats, void* hip_stream);
+
+/*
+ * The same forward pass with the Q quantization fused into the attention kernel.  [HiFA4
+ * Abstract: the Smooth-QK rescale is element-wise and fusible.]  q is FP16 [B, Hq, Lq, d] and s
+ * the Smooth-QK scales [Hkv, d] (device, or NULL for no rescale); each work-group rescales and
+ * quantizes the query rows it serves exactly as hifa4_quantize_qkv would, in registers, so no
+ * Q-hat is written to or read from memory.  The output is bit-identical to hifa4_quantize_qkv
+ * (with the same s) followed by hifa4_attention_fwd; every other argument, the workspace rules
+ * and the errors are those of hifa4_attention_fwd.
+ */
+hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
+                                     const float* s, const void* k_codes, const void* k_scales,
+                                     const void* v_codes, const void* v_scales, void* out, void* workspace,
+                                     size_t workspace_bytes, float* tile_stats, void* hip_stream);
 
 /* Static description of a status code. */
 const char* hifa4_status_string(hifa4_status status);

@@ -65,7 +65,15 @@ def run_case(q, k, v, causal, kv_tile, normalizer=A.P_REORDERED, alpha=0.5, cali
     splits_used = hf.decode_num_splits(dims, hf.make_opts(causal, normalizer, kv_tile, num_splits))
     r = hf.attention_fwd(res, dims, causal, normalizer, kv_tile, num_splits, tile_stats=True if stats else None)
     out, st = (r if stats else (r, None))
+    # the fused-Q entry point must reproduce the two-call path bit for bit
+    kv_only = {n: res[n] for n in NAMES[2:]}
+    r16 = hf.attention_fwd(kv_only, dims, causal, normalizer, kv_tile, num_splits, tile_stats=True if stats else None,
+                           q16=(to_dev(q), to_dev(s) if s is not None else None))
+    out16, st16 = (r16 if stats else (r16, None))
     torch.cuda.synchronize()
+    assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q output differs"
+    if stats:
+        assert torch.equal(st16, st), "fused-Q tile statistics differ"
     diag = A.Diag()
     want = A.attention_p(qq, causal, kv_tile, normalizer, num_splits=splits_used if lq == 1 else 1, diag=diag)
     return out.cpu().numpy(), want, qq, diag, (st.cpu().numpy() if st is not None else None)

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -38,6 +38,30 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings(L):
     assert L.hifa4_status_string(0) == b"ok"
     assert L.hifa4_status_string(5) == b"HIP runtime error"
+    assert b"16-byte" in L.hifa4_status_string(6)
+
+
+def test_misaligned_device_pointers_are_rejected(L):
+    dims = hf.make_dims(1, 4, 2, 128, 64, 64)
+    ok, off = ctypes.c_void_p(256), ctypes.c_void_p(264)  # never dereferenced
+    for i in range(7):
+        args = [ok] * 7
+        args[i] = off
+        st = L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(hf.make_opts(causal=True)), *args, None, 0, None, None)
+        assert st == 6 and b"aligned" in L.hifa4_last_error(), i
+    for i in range(8):  # fused-Q entry point: q, s, K-hat, V-hat, out, workspace
+        args = [ok] * 8
+        args[i] = off
+        st = L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(hf.make_opts(causal=True)), *args, 0, None, None)
+        assert st == 6, i
+    args = [ok] * 8
+    args[0] = None  # q is required; s may be NULL
+    assert L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(hf.make_opts()), *args, 0, None, None) == 1
+    for i in range(11):
+        args = [ok] * 11
+        args[i] = off
+        st = L.hifa4_quantize_qkv(ctypes.byref(dims), *args, None)
+        assert st == 6, i
 
 
 def test_attention_rejects_bad_arguments_without_launching(L):

@@ -47,7 +47,11 @@ def run_full(cfg_id, heads, n_rows, normalizer=A.P_REORDERED):
     res = hf.quantize_qkv(q, k, v, torch.from_numpy(s).cuda(), torch.from_numpy(inv).cuda(), dims=dims)
     splits = hf.decode_num_splits(dims, hf.make_opts(cfg["causal"], normalizer, cfg["kv_tile"], 0))
     out = hf.attention_fwd(res, dims, cfg["causal"], normalizer, cfg["kv_tile"])
+    # the launch bench.py times: K-hat, V-hat from the quantizer, Q quantized inside the kernel
+    out16 = hf.attention_fwd(res, dims, cfg["causal"], normalizer, cfg["kv_tile"],
+                             q16=(q, torch.from_numpy(s).cuda()))
     torch.cuda.synchronize()
+    assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q output differs"
     rng = np.random.default_rng(7000 + cfg_id)
     worst = 0.0
     for (b, h) in heads:
