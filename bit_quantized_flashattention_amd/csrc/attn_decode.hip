@@ -19,7 +19,7 @@ struct TileOps {
   uint4 k[8][KSTEPS];   // K-hat A operands of the 8 score MFMAs (2 contraction steps for d = 256)
   uint2 ksc[KSTEPS];    // scale bytes of the 8 keys of the lane's MFMA row (byte t: MFMA t)
   uint4 v[CB];          // V-hat^T A operands of the channel blocks
-  uint32_t vsc[CB / 4]; // scale bytes of the lane's CB channels (byte cb: block cb)
+  uint32_t vsc[CB / 4]; // scale bytes of the lane's CB channels (byte cb: channel 16 cb + col)
 };
 
 // HBM -> registers: this lane's MFMA operands of the tile at key k0 (see score_row_key and the
@@ -50,7 +50,7 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
   const int64_t row = (k0 / kBlock + g) * D;  // block-major V-hat: cells (32-key block, channel)
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
-    t.v[cb] = okv ? *reinterpret_cast<const uint4*>(vc + (row + CB * col + cb) * 16) : make_uint4(0u, 0u, 0u, 0u);
+    t.v[cb] = okv ? *reinterpret_cast<const uint4*>(vc + (row + 16 * cb + col) * 16) : make_uint4(0u, 0u, 0u, 0u);
   if constexpr (CB == 4) {
     t.vsc[0] = okv ? *reinterpret_cast<const uint32_t*>(vs + row + CB * col) : 0x7F7F7F7Fu;
   } else if constexpr (CB == 8) {
@@ -188,23 +188,12 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 
   if (!live_col) return;
   const int64_t part = ((int64_t)b * a.heads_q + h) * a.num_splits + split;
-  // register i of block cb holds channel CB (4 g + i) + cb: CB adjacent channels per i
-  uint16_t* po = a.part_o + part * D + CB * 4 * g;
+  // register i of block cb holds channel 16 cb + 4 g + i: 4 adjacent channels per block
+  uint16_t* po = a.part_o + part * D + 4 * g;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    uint32_t w[CB / 2];
-#pragma unroll
-    for (int cb = 0; cb < CB; cb += 2) {
-      // the FP16 bits of register i: half (i & 1) of the pair o[cb][i / 2]
-      const uint32_t p0 = __builtin_bit_cast(uint32_t, o[cb][i >> 1]);
-      const uint32_t p1 = __builtin_bit_cast(uint32_t, o[cb + 1][i >> 1]);
-      const uint32_t h0 = (i & 1) ? (p0 >> 16) : (p0 & 0xFFFFu);
-      const uint32_t h1 = (i & 1) ? (p1 >> 16) : (p1 & 0xFFFFu);
-      w[cb / 2] = h0 | (h1 << 16);
-    }
-#pragma unroll
-    for (int j = 0; j < CB / 2; j += 2) *reinterpret_cast<uint2*>(po + CB * i + 2 * j) = make_uint2(w[j], w[j + 1]);
-  }
+  for (int cb = 0; cb < CB; cb++)
+    *reinterpret_cast<uint2*>(po + 16 * cb) =
+        make_uint2(__builtin_bit_cast(uint32_t, o[cb][0]), __builtin_bit_cast(uint32_t, o[cb][1]));
   if (g == 0) {
     a.part_ml[part * 2 + 0] = __builtin_bit_cast(uint16_t, (_Float16)m);
     a.part_ml[part * 2 + 1] = __builtin_bit_cast(uint16_t, (_Float16)l);

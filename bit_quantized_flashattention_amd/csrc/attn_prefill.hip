@@ -85,7 +85,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // its section at key 0.  Positions are inverted here: a lane loads whatever HBM bytes belong at
 // its LDS position.  The code loads are exactly the operands of one MFMA: lane (g, col) of score
 // MFMA t fetches chunk g of key score_row_key(t, col); lane (g, col) of PV MFMA cb fetches the
-// 32-key block g of channel CB col + cb.  The scale loads copy the block-plane K-hat rows and the
+// 32-key block g of channel 16 cb + col.  The scale loads copy the block-plane K-hat rows and the
 // V-hat block rows of the tile.
 struct LoadOp {
   int sec;
@@ -109,7 +109,7 @@ __device__ __forceinline__ LoadOp load_op(int i, int lane, int lk32) {
     const int cb = i - C::kKCInstr;
     op.sec = 1;
     op.lds = C::kVC + cb * 1024;
-    op.voff = (g * D + C::kCB * col + cb) * 16;  // block-major V-hat: (32-key block, channel) cells
+    op.voff = (g * D + 16 * cb + col) * 16;  // block-major V-hat cells (32-key block g, channel 16 cb + col)
   } else if (i < C::kKCInstr + C::kVCInstr + C::kKSInstr) {
     const int q = i - C::kKCInstr - C::kVCInstr;
     const int pos = q * 256 + 4 * lane;  // [block][key] rows of 128 bytes
@@ -428,10 +428,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
           }
         }
       }
-      // ---- O^T += V-hat^T P-hat^T per channel block (PV MFMA cb takes channel CB r + cb as row
+      // ---- O^T += V-hat^T P-hat^T per channel block (PV MFMA cb takes channel 16 cb + r as row
       // r; operands in lane order); FP16 state update
       const uint8_t* vbase = T + v_lane_off;
-      // the lane's CB V-hat scale bytes (byte cb serves channel block cb)
+      // the lane's CB V-hat scale bytes (byte cb: channel 16 cb + col, adjacent in the layout)
       uint32_t vsw[CB / 4];
       if constexpr (CB == 4) {
         vsw[0] = *reinterpret_cast<const uint32_t*>(T + vs_lane_off);
@@ -477,11 +477,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
     __syncthreads();
   }
 
-  // ---- epilogue: out = fp16(O / l); register i of block cb holds channel CB (4 g + i) + cb
+  // ---- epilogue: out = fp16(O / l); register i of block cb holds channel 16 cb + 4 g + i
   const int q = q0 + col;
   if (!wave_live || q >= lq) return;
   uint16_t* out = a.out + ((int64_t)b * a.heads_q + h) * (int64_t)lq * D;
-  write_out_row<CB>(out + (int64_t)q * D + CB * 4 * g, o, (float)l);
+  write_out_row<CB>(out + (int64_t)q * D + 4 * g, o, (float)l);
 }
 
 int gcd_int(int x, int y) {

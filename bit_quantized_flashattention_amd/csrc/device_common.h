@@ -189,9 +189,10 @@ __device__ __forceinline__ int score_row_key(int t, int r) { return 32 * (r >> 2
 __device__ __host__ constexpr int s_key(int k) { return 8 * (k & 3) + (k >> 2); }
 // accumulator index holding key offset j of the block
 __device__ __host__ constexpr int s_index(int j) { return 4 * (j & 7) + (j >> 3); }
-// PV MFMA cb takes channel chi(cb, r) = CB r + cb as its row r, so lane (g, col) needs the scales
-// of channels CB col .. CB col + CB - 1 (adjacent) and its output register i holds channel
-// CB (4 g + i) + cb of its query.
+// PV MFMA cb takes channel chi(cb, r) = 16 cb + r as its row r: the 16 lanes of a lane group
+// read 16 adjacent V-hat cells.  Lane (g, col) needs the scales of channels col, 16 + col, ...,
+// which the V-hat scale layout keeps adjacent, and its output register i of block cb holds
+// channel 16 cb + 4 g + i of its query.
 
 // P-hat codes of a lane's 32 keys: E2M1 of rn16(2^rn16(fma32(s_k, C, -(m + e)))), packed two
 // per byte in key order (key 2j of the block in the low nibble of byte j); a score of -inf
@@ -245,8 +246,8 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
 }
 
 // Writes one query's output row fp16(O / l) from the FP16 state of CB channel blocks: register i
-// (i = 0..3) of block cb holds channel CB (4 g + i) + cb, so for each i the CB values are
-// adjacent channels; dst points at channel 4 g CB of the row.
+// (i = 0..3) of block cb holds channel 16 cb + 4 g + i, so each block gives 4 adjacent channels;
+// dst points at channel 4 g of the row.
 //
 // The quotient: fp16(x / l) for FP16 values x and l > 0 equals the FP16 rounding of the IEEE
 // FP32 quotient.  Here q = x r with r ~ 1/l (hardware reciprocal, ~1 ulp) is corrected once with
@@ -264,21 +265,15 @@ template <int CB>
 __device__ __forceinline__ void write_out_row(uint16_t* dst, const h2 (*o)[2], float l) {
   const float r = __builtin_amdgcn_rcpf(l);
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    uint32_t w[CB / 2];
+  for (int cb = 0; cb < CB; cb++) {
+    uint32_t w[2];
 #pragma unroll
-    for (int cb = 0; cb < CB; cb += 2) {
-      const float x0 = quot_h((float)o[cb][i >> 1][i & 1], l, r);
-      const float x1 = quot_h((float)o[cb + 1][i >> 1][i & 1], l, r);
-      w[cb / 2] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+    for (int j = 0; j < 2; j++) {
+      const float x0 = quot_h((float)o[cb][j][0], l, r);
+      const float x1 = quot_h((float)o[cb][j][1], l, r);
+      w[j] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
     }
-    uint16_t* d = dst + CB * i;
-    if constexpr (CB == 4) {
-      *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < CB / 2; j += 4) *reinterpret_cast<uint4*>(d + 2 * j) = make_uint4(w[j], w[j + 1], w[j + 2], w[j + 3]);
-    }
+    *reinterpret_cast<uint2*>(dst + 16 * cb) = make_uint2(w[0], w[1]);
   }
 }
 

@@ -84,10 +84,12 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
     out.y = pack8_fp4(v + 8, sc);
     out.z = pack8_fp4(v + 16, sc);
     out.w = pack8_fp4(v + 24, sc);
-    // block-major V-hat: [bh][token block][channel] -> 16 code bytes, one scale byte
-    const int64_t cell = (bh * (a.len32 / kBlock) + t0 / kBlock + jb) * D + ch;
-    *reinterpret_cast<uint4*>(a.codes + cell * 16) = out;
-    a.scales[cell] = (uint8_t)(e + 127);
+    // block-major V-hat: [bh][token block][channel] -> 16 code bytes; the block's scale bytes
+    // are stored channel ch at (D/16) (ch % 16) + ch / 16, so the D/16 channels ch, ch + 16, ...
+    // that one MFMA lane serves have adjacent scale bytes
+    const int64_t blk_row = (bh * (a.len32 / kBlock) + t0 / kBlock + jb) * D;
+    *reinterpret_cast<uint4*>(a.codes + (blk_row + ch) * 16) = out;
+    a.scales[blk_row + (D / 16) * (ch % 16) + ch / 16] = (uint8_t)(e + 127);
   }
 }
 

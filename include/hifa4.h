@@ -22,7 +22,9 @@
  *   v_codes  u8   [B, Hkv, Lk32/32, d, 16]   v_scales  u8   [B, Hkv, Lk32/32, d]
  *                 (V-hat is blocked along tokens and stored block-major: for each block of 32
  *                 tokens, the 16 code bytes of channel 0, then channel 1, ...; a key tile is one
- *                 contiguous run of bytes.  Lk32 = Lk rounded up to 32, tail tokens are 0)
+ *                 contiguous run of bytes.  The scale bytes of a block are stored channel c at
+ *                 position (d/16) * (c % 16) + c / 16.  Lk32 = Lk rounded up to 32, tail tokens
+ *                 are 0)
  *   out      FP16 [B, Hq,  Lq, d]
  *   s, inv_s FP32 [Hkv, d]                   (query head h uses KV head h / (Hq/Hkv))
  *

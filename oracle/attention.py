@@ -140,12 +140,15 @@ class Quantized:
         are stored as block planes: for each 32-channel block, the scale bytes of all keys,
         padded with zero bytes to a multiple of 32 keys ([B, Hkv, d/32, Lk32]).  V-hat is stored
         token-block major: for each 32-token block, the 16 code bytes of every channel
-        ([B, Hkv, Lk32/32, d, 16]) and the scale bytes of every channel ([B, Hkv, Lk32/32, d]).
+        ([B, Hkv, Lk32/32, d, 16]) and the scale bytes of every channel ([B, Hkv, Lk32/32, d]),
+        the scale bytes in the order of channels 0, 16, 32, ..., 1, 17, ... (channel c at
+        position (d/16) * (c % 16) + c // 16).
         """
         b, hkv, d, lk32 = self.vc.shape
         lk = self.kc.shape[2]
         vcode = mx.pack_codes(self.vc).reshape(b, hkv, d, lk32 // 32, 16).transpose(0, 1, 3, 2, 4)
-        vscale = np.swapaxes(mx.scale_bytes(self.ve), 2, 3)
+        vscale = np.swapaxes(mx.scale_bytes(self.ve), 2, 3)  # [B, Hkv, Lk32/32, d], channel order
+        vscale = vscale.reshape(b, hkv, lk32 // 32, d // 16, 16).transpose(0, 1, 2, 4, 3).reshape(b, hkv, lk32 // 32, d)
         kscale = np.zeros((b, hkv, d // 32, lk32), dtype=np.uint8)
         kscale[..., :lk] = np.swapaxes(mx.scale_bytes(self.ke), 2, 3)
         return (mx.pack_codes(self.qc), mx.scale_bytes(self.qe), mx.pack_codes(self.kc),
