@@ -273,7 +273,7 @@ def main():
             "head_dim": cfg["d"], "normalizer": "p_reordered", "smooth_qk_gate": pre["gate"],
         },
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": traffic_for("prefill"),
+                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": traffic_for("prefill") if args.workload == "prefill" else None,
                      "kernel_ms": round(pre["attn_ms"], 4)},
     }
     if not args.no_cpu_baseline:
