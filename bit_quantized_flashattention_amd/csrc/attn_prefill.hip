@@ -395,9 +395,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
         if (CAUSAL && q + shift < lim) lim = q + shift;
         if (k0 + bc - 1 < lim) lim = k0 + bc - 1;
         if (q >= lq) lim = -1;
+        const int rel = lim - kb;  // key offset s_key(k) of the lane's block is visible iff <= rel
 #pragma unroll
         for (int k = 0; k < 32; k++) {
-          s[k] = (kb + s_key(k) <= lim) ? s[k] : -INFINITY;
+          s[k] = (s_key(k) <= rel) ? s[k] : -INFINITY;
           bmax = fmaxf(bmax, s[k]);
         }
       }

@@ -166,12 +166,25 @@ struct RowStep {
   float neg_big_m;  // -(m_new + e): log2-domain offset of the scores relative to 2^e
 };
 
+// max of two FP32 values that are never NaN, as one v_max_f32 (fmaxf would first quiet operands
+// the compiler cannot prove canonical, such as cross-lane results and loop-carried values)
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   RowStep r;
-  r.m_new = fmaxf(m, __builtin_ceilf(rmax * C));
-  const float al = (m == -INFINITY) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - r.m_new));
-  r.alpha = (_Float16)al;
-  const float mm = (r.m_new == -INFINITY) ? 0.0f : r.m_new;
+  r.m_new = max_nn(m, __builtin_ceilf(rmax * C));
+  // 2^(m - m_new) straight in FP16: exact down to 2^-24; below that (rn16 gives 0, 2^-25 being
+  // a tie to even) and while m = -inf (d = -inf or NaN) the exponent -64 gives 0
+  const float d = m - r.m_new;
+  const int dm = d >= -24.0f ? (int)d : -64;
+  r.alpha = __builtin_ldexpf16((_Float16)1.0f, dm);
+  // m_new = -inf only for a row with no visible key yet: any finite stand-in below every real
+  // m keeps e = -127 and every code 0
+  const float mm = max_nn(r.m_new, -0x1p100f);
   r.e = tile_exponent(__builtin_fmaf(rmax, C, -mm));
   r.neg_big_m = -(mm + r.e);
   return r;
@@ -301,9 +314,9 @@ __device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, uint32_t sa, const u
 // lane: v_permlane16_swap pairs rows (0,1) and (2,3), v_permlane32_swap pairs halves.
 __device__ __forceinline__ float group_max4(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 // (x0 + x1) + (x2 + x3) with x_g the value of lane group g, the same bits in every lane
 __device__ __forceinline__ float group_sum4(float x) {
