@@ -88,6 +88,14 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   int t_hi = t_lo + a.tiles_per_split;
   if (t_hi > a.n_tiles) t_hi = a.n_tiles;
 
+  const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);
+  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk32 * (D / kBlock);
+  const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / 2);
+  const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / kBlock);
+  // the first tile is put in flight before the query is loaded, so the two latencies overlap
+  TileOps<D> cur, nxt;
+  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
+
   // Q-hat^T operand: column = query head, K-chunk g
   uint4 qreg[KSTEPS];
   uint32_t qsc[KSTEPS];
@@ -114,10 +122,6 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
     }
   }
 
-  const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);
-  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk32 * (D / kBlock);
-  const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / 2);
-  const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / kBlock);
   const float C = a.c_log2;
   const int64_t shift = lk - 1;
 
@@ -127,8 +131,6 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   _Float16 l = (_Float16)0.0f;
   float m = -INFINITY;
 
-  TileOps<D> cur, nxt;
-  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
   for (int tile = t_lo; tile < t_hi; tile++) {
     const int64_t k0 = (int64_t)tile * bc;
     if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, k0 + bc, lk, lk32, bc, col, g);

@@ -93,6 +93,24 @@ def test_decode_split_kv(d, splits, normalizer):
     compare_out(got, want, "decode-d%d-s%d" % (d, splits))
 
 
+def test_decode_workspace_reuse_and_head_chunks():
+    """GQA group of 32 (two 16-head chunks per KV head, two split waves per (batch, KV head,
+    split)); repeated calls on one workspace give identical outputs."""
+    import torch
+    cfg, q, k, v, cal = gen(1, B=2, Hq=32, Hkv=1, Lq=1, Lk=777, d=128)
+    print("case decode group 32, workspace reuse", flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, calib=cal, num_splits=3)
+    compare_out(got, want, "decode-g32-s3")
+    res = gpu_quantize(q, k, v, None, None)
+    dims = hf.make_dims(2, 32, 1, 128, 1, 777)
+    opts = hf.make_opts(True, 0, 128, 3)
+    n = hf.attention_workspace_bytes(dims, opts)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    outs = [hf.attention_fwd(res, dims, True, 0, 128, 3, workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
 def test_tile_stats_match_oracle():
     cfg, q, k, v, cal = gen(1, B=1, Hq=4, Hkv=1, Lq=200, Lk=200)
     print("case stats", flush=True)
