@@ -111,6 +111,21 @@ def test_decode_workspace_reuse_and_head_chunks():
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("b,hq,hkv,lq,lk,d,causal,kv_tile", [
+    (1, 4, 1, 1, 1, 128, True, 128),     # decode over a single key
+    (2, 2, 2, 1, 31, 64, False, 64),     # decode, non-causal flag, less than one scale block
+    (1, 2, 1, 3, 3, 64, True, 64),       # three-row causal prefill
+    (1, 2, 2, 2, 40, 256, False, 64),    # two rows, one partial tile pair, d = 256
+    (1, 1, 1, 33, 31, 128, False, 128),  # more queries than keys (non-causal)
+    (3, 6, 3, 17, 129, 128, True, 128),  # one key past a tile, rows past a 16-row block
+])
+def test_tiny_and_ragged_shapes(b, hq, hkv, lq, lk, d, causal, kv_tile):
+    cfg, q, k, v, cal = gen(1 if d != 256 else 3, B=b, Hq=hq, Hkv=hkv, Lq=lq, Lk=lk, d=d)
+    print("case tiny", b, hq, hkv, lq, lk, d, causal, kv_tile, flush=True)
+    got, want, *_ = run_case(q, k, v, causal, kv_tile, calib=cal)
+    compare_out(got, want, "tiny-%d-%d-%d" % (lq, lk, d))
+
+
 def test_tile_stats_match_oracle():
     cfg, q, k, v, cal = gen(1, B=1, Hq=4, Hkv=1, Lq=200, Lk=200)
     print("case stats", flush=True)
