@@ -215,7 +215,10 @@ __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, 
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    uint32_t x = 0;
+    // every byte of x is written by one of the four conversions below, so it needs no initial
+    // value (an empty asm hands over whatever the register holds, instead of a move of 0)
+    uint32_t x;
+    asm volatile("" : "=v"(x));
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int k = 8 * q + 2 * j;  // key offsets k, k + 1
