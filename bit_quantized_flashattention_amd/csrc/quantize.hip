@@ -11,13 +11,29 @@ namespace hifa4 {
 // Consecutive threads own consecutive blocks, so loads and stores are contiguous per wave.
 // K-hat scales are written as block planes [B*H, d/32, len32] (one row of key scales per
 // 32-channel block, what the attention kernels stage per tile); threads past the last key of
-// a row write the zero scale bytes of the padding.
+// a row write the zero scale bytes of the padding.  When all rows of a work-group belong to one
+// (batch, head), its Smooth-QK scale row is staged in LDS once instead of every thread reading
+// its 128 bytes of scales through the vector memory path.
 template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   constexpr int NB = D / kBlock;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float s_row[D];
   const int64_t n_rows = PLANES ? a.rows / a.len * a.len32 : a.rows;
-  if (t >= n_rows * NB) return;
+  const int64_t n_items = n_rows * NB;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x;
+  const int64_t t = t0 + threadIdx.x;
+  // (batch, head) index of the work-group's first and last row; uniform across the group
+  const int64_t t_last = (t0 + blockDim.x < n_items ? t0 + blockDim.x : n_items) - 1;
+  const int64_t rows_per_bh = PLANES ? a.len32 : a.len;
+  const int64_t bh_first = t0 / NB / rows_per_bh, bh_last = t_last / NB / rows_per_bh;
+  const bool staged = a.scale != nullptr && bh_first == bh_last;
+  if (staged) {
+    const int h = (int)(bh_first % a.heads);
+    const float* src = a.scale + (int64_t)(h / a.heads_per_scale_row) * D;
+    for (int i = threadIdx.x; i < D; i += blockDim.x) s_row[i] = src[i];
+    __syncthreads();
+  }
+  if (t >= n_items) return;
   const int blk = (int)(t % NB);
   int64_t row = t / NB;
   uint8_t* scale_dst;
@@ -32,13 +48,18 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   } else {
     scale_dst = a.scales + row * NB + blk;
   }
-  const float* sc = nullptr;
-  if (a.scale != nullptr) {
+  Block32In in;
+  load_block32(a.x + row * D + blk * kBlock, nullptr, in);
+  if (staged) {
+    const float4* ls = reinterpret_cast<const float4*>(s_row + blk * kBlock);
+#pragma unroll
+    for (int i = 0; i < 8; i++) in.s[i] = ls[i];
+  } else if (a.scale != nullptr) {
     const int h = (int)((row / a.len) % a.heads);
-    sc = a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock;
+    load_block32(nullptr, a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock, in);
   }
   uint4 out;
-  const uint32_t e8 = quantize_block32(a.x + row * D + blk * kBlock, sc, &out);
+  const uint32_t e8 = quantize_loaded32(in, a.scale != nullptr, &out);
   *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + blk * 16) = out;
   *scale_dst = (uint8_t)e8;
 }
