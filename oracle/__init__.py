@@ -22,6 +22,8 @@ Modules:
   fp         exact FP32 / FP16 rounding helpers (fma, two-operand sums, fract)
   mx         E2M1 codes with a power-of-two scale per 32-element block
   smooth     Smooth-QK calibration and the element-wise rescale
+  rope       the FP32 rotate-half RoPE of the fused prologue (RoPE, then Smooth-QK,
+             then quantization, from pre-RoPE FP16 inputs)
   attention  the tiled recurrence with P-Reordering, split-KV merge, the
              inconsistent-normalizer variant, epsilon statistics and the
              unquantized FP32 reference

@@ -84,16 +84,27 @@ def _rope(x, positions, theta):
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
+def rope_table(theta, n_pos, d):
+    """cos and sin of the rotate-half RoPE angles, FP32 [n_pos, d/2]: angle (p, i) = p * theta**(-2i/d),
+    computed in FP64 and rounded once.  These tables are an input of the fused RoPE prologue, as a
+    model runtime's cached cos/sin would be."""
+    half = d // 2
+    omega = theta ** (-2.0 * np.arange(half) / d)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * omega[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def _draw(rng, shape):
     return rng.standard_normal(shape, dtype=np.float32).astype(np.float64)
 
 
-def make_qkv(cfg, batch_slice=None, seed_offset=0):
+def make_qkv(cfg, batch_slice=None, seed_offset=0, pre_rope=False):
     """Q [B, Hq, Lq, d], K, V [B, Hkv, Lk, d] as float16 arrays.
 
     ``batch_slice`` (start, stop) draws only those batch entries, each from its
     own child seed, so large configs can be generated in chunks with the same
-    result as a whole draw.
+    result as a whole draw.  ``pre_rope`` returns Q and K before the rotation
+    (the same draws, rounded to FP16), the input of the fused RoPE prologue.
     """
     b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
     lo, hi = batch_slice if batch_slice is not None else (0, b_n)
@@ -107,8 +118,9 @@ def make_qkv(cfg, batch_slice=None, seed_offset=0):
         q = _draw(rng, (hq, lq, d))
         k = _draw(rng, (hkv, lk, d)) * gain[:, None, :]
         v = _draw(rng, (hkv, lk, d))
-        qs.append(_rope(q, qpos, cfg["rope_theta"]).astype(np.float16))
-        ks.append(_rope(k, kpos, cfg["rope_theta"]).astype(np.float16))
+        theta = None if pre_rope else cfg["rope_theta"]
+        qs.append(_rope(q, qpos, theta).astype(np.float16))
+        ks.append(_rope(k, kpos, theta).astype(np.float16))
         vs.append(v.astype(np.float16))
     return np.stack(qs), np.stack(ks), np.stack(vs)
 
@@ -129,12 +141,12 @@ def small(cfg_id, **override):
     return config(cfg_id, **override)
 
 
-def make_qkv_device(cfg, device="cuda", with_q=True, with_kv=True):
+def make_qkv_device(cfg, device="cuda", with_q=True, with_kv=True, pre_rope=False):
     """Same distributions as make_qkv, drawn on the GPU with torch's seeded generator.
 
     Used for the full-size workloads (the decode cache alone is 8.6 GB of FP16); the
     values differ from make_qkv's (another random stream) but the recipe is identical.
-    Returns float16 CUDA tensors (None for parts not requested).
+    Returns float16 CUDA tensors (None for parts not requested); ``pre_rope`` as in make_qkv.
     """
     import torch
     b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
@@ -143,7 +155,7 @@ def make_qkv_device(cfg, device="cuda", with_q=True, with_kv=True):
     gain = torch.tensor(_channel_gain(cfg, hkv, d), dtype=torch.float32, device=device)
 
     def rope(x, positions):
-        if cfg["rope_theta"] is None:
+        if cfg["rope_theta"] is None or pre_rope:
             return x
         half = d // 2
         i = torch.arange(half, device=device, dtype=torch.float64)
