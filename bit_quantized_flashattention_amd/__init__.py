@@ -49,6 +49,8 @@ def lib():
         L.hifa4_calibrate.restype = ctypes.c_int
         L.hifa4_quantize_qkv.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 11
         L.hifa4_quantize_qkv.restype = ctypes.c_int
+        L.hifa4_quantize_qkv_rope.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 7 + [ctypes.c_int64] + [_vp] * 7
+        L.hifa4_quantize_qkv_rope.restype = ctypes.c_int
         L.hifa4_decode_num_splits.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)]
         L.hifa4_decode_num_splits.restype = ctypes.c_int32
         L.hifa4_attention_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)]
@@ -151,6 +153,40 @@ def quantize_qkv(q=None, k=None, v=None, s=None, inv_s=None, dims=None, out=None
         raise ValueError("pass both s and inv_s or neither")
     _check(lib().hifa4_quantize_qkv(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(inv_s),
+        _ptr(res.get("q_codes") if q is not None else None), _ptr(res.get("q_scales") if q is not None else None),
+        _ptr(res.get("k_codes") if k is not None else None), _ptr(res.get("k_scales") if k is not None else None),
+        _ptr(res.get("v_codes") if v is not None else None), _ptr(res.get("v_scales") if v is not None else None),
+        _stream(stream)))
+    return res
+
+
+def quantize_qkv_rope(q=None, k=None, v=None, s=None, inv_s=None, rope_cos=None, rope_sin=None, dims=None,
+                      out=None, stream=None):
+    """RoPE + Smooth-QK + 4-bit quantization of pre-RoPE q, k (and plain v) on the GPU.
+
+    rope_cos, rope_sin: CUDA float32 [n_pos, d/2] tables (n_pos >= Lk).  Otherwise as quantize_qkv.
+    """
+    import torch
+    if dims is None:
+        b, hq, lq, d = q.shape
+        hkv, lk = k.shape[1], k.shape[2]
+        dims = make_dims(b, hq, hkv, d, lq, lk)
+    for t in (q, k, v):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float16 or not t.is_contiguous()):
+            raise ValueError("q, k, v must be contiguous CUDA float16 tensors")
+    for t in (rope_cos, rope_sin):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("rope tables must be contiguous CUDA float32 tensors")
+    shapes = quantized_shapes(dims.batch, dims.heads_q, dims.heads_kv, dims.head_dim, dims.len_q, dims.len_kv)
+    dev = next(t for t in (q, k, v) if t is not None).device
+    res = dict(out) if out is not None else {}
+    for name, shp in shapes.items():
+        src = {"q": q, "k": k, "v": v}[name[0]]
+        if src is not None and name not in res:
+            res[name] = torch.empty(shp, dtype=torch.uint8, device=dev)
+    n_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    _check(lib().hifa4_quantize_qkv_rope(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(inv_s), _ptr(rope_cos), _ptr(rope_sin), n_pos,
         _ptr(res.get("q_codes") if q is not None else None), _ptr(res.get("q_scales") if q is not None else None),
         _ptr(res.get("k_codes") if k is not None else None), _ptr(res.get("k_scales") if k is not None else None),
         _ptr(res.get("v_codes") if v is not None else None), _ptr(res.get("v_scales") if v is not None else None),

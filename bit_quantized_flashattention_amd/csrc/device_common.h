@@ -70,30 +70,10 @@ __device__ __forceinline__ void load_block32(const uint16_t* x, const float* s, 
   }
 }
 
-// Smooth-QK rescale and 4-bit quantization of one loaded block (scaled: apply in.s).  Each value
-// becomes fp32(x * s) (one rounding; contraction is off), the block exponent comes from the
-// largest magnitude, and the codes are RNE onto E2M1 relative to 2^e.  Returns the E8M0 scale
-// byte (e + 127); the 16 code bytes go to *codes (element 2i in the low nibble of byte i).
-__device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool scaled, uint4* codes) {
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t w[4] = {in.x[i].x, in.x[i].y, in.x[i].z, in.x[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v[i * 8 + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFF));
-      v[i * 8 + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
-    }
-  }
-  if (scaled) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      v[4 * i + 0] = v[4 * i + 0] * in.s[i].x;
-      v[4 * i + 1] = v[4 * i + 1] * in.s[i].y;
-      v[4 * i + 2] = v[4 * i + 2] * in.s[i].z;
-      v[4 * i + 3] = v[4 * i + 3] * in.s[i].w;
-    }
-  }
+// 4-bit quantization of 32 FP32 values: the block exponent comes from the largest magnitude and
+// the codes are RNE onto E2M1 relative to 2^e.  Returns the E8M0 scale byte (e + 127); the 16
+// code bytes go to *codes (element 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t quantize_values32(const float* v, uint4* codes) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
@@ -104,6 +84,36 @@ __device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool 
   codes->z = pack8_fp4(v + 16, scale);
   codes->w = pack8_fp4(v + 24, scale);
   return (uint32_t)(e + 127);
+}
+
+// The 32 FP16 values of a loaded block as FP32 (exact).
+__device__ __forceinline__ void unpack_block32(const Block32In& in, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w[4] = {in.x[i].x, in.x[i].y, in.x[i].z, in.x[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[i * 8 + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFF));
+      v[i * 8 + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+    }
+  }
+}
+
+// Smooth-QK rescale and 4-bit quantization of one loaded block (scaled: apply in.s).  Each value
+// becomes fp32(x * s) (one rounding; contraction is off), then quantize_values32.
+__device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool scaled, uint4* codes) {
+  float v[32];
+  unpack_block32(in, v);
+  if (scaled) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[4 * i + 0] = v[4 * i + 0] * in.s[i].x;
+      v[4 * i + 1] = v[4 * i + 1] * in.s[i].y;
+      v[4 * i + 2] = v[4 * i + 2] * in.s[i].z;
+      v[4 * i + 3] = v[4 * i + 3] * in.s[i].w;
+    }
+  }
+  return quantize_values32(v, codes);
 }
 
 // Both steps for one block (see load_block32 and quantize_loaded32).

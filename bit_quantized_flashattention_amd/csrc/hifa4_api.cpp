@@ -211,6 +211,49 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
   return ok();
 }
 
+hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, const void* k, const void* v,
+                                     const float* s, const float* inv_s, const float* rope_cos,
+                                     const float* rope_sin, int64_t rope_positions, void* q_codes,
+                                     void* q_scales, void* k_codes, void* k_scales, void* v_codes,
+                                     void* v_scales, void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  if ((s == nullptr) != (inv_s == nullptr)) return fail(HIFA4_ERR_NULL, "quantize: pass both s and inv_s or neither");
+  if ((q || k) && (!rope_cos || !rope_sin)) return fail(HIFA4_ERR_NULL, "quantize: RoPE tables are NULL");
+  if (q && (!q_codes || !q_scales)) return fail(HIFA4_ERR_NULL, "quantize: q outputs are NULL");
+  if (k && (!k_codes || !k_scales)) return fail(HIFA4_ERR_NULL, "quantize: k outputs are NULL");
+  if (v && (!v_codes || !v_scales)) return fail(HIFA4_ERR_NULL, "quantize: v outputs are NULL");
+  if (q && dims->len_q > dims->len_kv)
+    return fail(HIFA4_ERR_SHAPE, "quantize: RoPE positions need len_q <= len_kv (query r sits at r + len_kv - len_q)");
+  if ((q || k) && rope_positions < dims->len_kv)
+    return fail(HIFA4_ERR_SHAPE, "quantize: the RoPE tables need at least len_kv positions");
+  if (!aligned16({q, k, v, s, inv_s, rope_cos, rope_sin, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales}))
+    return fail(HIFA4_ERR_ALIGNMENT, "quantize: device pointers must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const int group = dims->heads_q / dims->heads_kv;
+  if (q) {
+    hifa4::QuantRopeArgs a{(const uint16_t*)q, s, rope_cos, rope_sin, dims->batch, dims->len_q, round32(dims->len_q),
+                           dims->len_kv - dims->len_q, dims->heads_q, group, dims->heads_kv, dims->head_dim, 0, 0,
+                           (uint8_t*)q_codes, (uint8_t*)q_scales};
+    hipError_t e = hifa4::launch_quantize_rope(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
+  }
+  if (k) {
+    hifa4::QuantRopeArgs a{(const uint16_t*)k, inv_s, rope_cos, rope_sin, dims->batch, dims->len_kv,
+                           round32(dims->len_kv), 0, dims->heads_kv, 1, dims->heads_kv, dims->head_dim, 1, 0,
+                           (uint8_t*)k_codes, (uint8_t*)k_scales};
+    hipError_t e = hifa4::launch_quantize_rope(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
+  }
+  if (v) {
+    hifa4::QuantVtArgs a{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
+                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales};
+    hipError_t e = hifa4::launch_quantize_vt(a, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize v: ") + hipGetErrorString(e));
+  }
+  return ok();
+}
+
 int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts) {
   if (check_dims(dims) != HIFA4_OK || check_opts(dims, opts) != HIFA4_OK) return 0;
   return resolve_splits(dims, opts);

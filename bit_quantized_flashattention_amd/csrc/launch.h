@@ -55,7 +55,26 @@ struct AttnArgs {
   float c_log2;         // fp32(log2(e) / sqrt(d))
 };
 
+struct QuantRopeArgs {
+  const uint16_t* x;    // FP16 [B, H, len, d], before RoPE
+  const float* scale;   // Smooth-QK FP32 [Hs, d] or nullptr
+  const float* rope_cos;  // FP32 [n_pos, d/2]
+  const float* rope_sin;
+  int64_t batch;
+  int64_t len;          // L
+  int64_t len32;        // L rounded up to 32 (block-plane scales)
+  int64_t pos0;         // RoPE position of token 0 (Lk - Lq for Q, 0 for K)
+  int32_t heads;        // H
+  int32_t heads_per_scale_row;  // query heads per KV head for Q (Hq/Hkv), 1 for K
+  int32_t scale_rows;   // Hs (rows of scale)
+  int32_t d;
+  int32_t block_planes; // 0: scales [rows, d/32] (Q-hat); 1: [B*H, d/32, len32] (K-hat), tail 0
+  int32_t pos_per_wg;   // positions per work-group (set by the launcher)
+  uint8_t* codes;       // [B*H*len, d/2]
+  uint8_t* scales;
+};
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s);
 hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);

@@ -114,6 +114,115 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
   }
 }
 
+// RoPE (FP32, rotate-half), Smooth-QK and 4-bit quantization of pre-RoPE rows, fused.  A
+// work-group serves pos_per_wg consecutive positions of one batch entry for all H heads, so the
+// cos/sin rows of those positions (and the Smooth-QK scale table when it is small) are staged in
+// LDS once and shared by every head.  An item is one (position, head, block pair j): channels
+// 32 j .. 32 j + 31 and their rotation partners 32 j + d/2 .. , so each item writes two
+// quantization blocks.  Rounding, as the rotation is defined for this prologue: each product
+// and each sum once in FP32, no fused multiply-add (contraction is off), then fp32(y * s).
+constexpr int kRopeMaxPos = 32;          // positions per work-group at most
+constexpr int kRopeMaxScaleFloats = 4096;  // Smooth-QK tables up to 16 KB are staged in LDS
+
+template <int D, bool PLANES>
+__global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
+  constexpr int NB = D / kBlock;
+  constexpr int NP = NB / 2;  // block pairs per row
+  constexpr int H2 = D / 2;
+  __shared__ __attribute__((aligned(16))) float s_cos[kRopeMaxPos * H2];
+  __shared__ __attribute__((aligned(16))) float s_sin[kRopeMaxPos * H2];
+  __shared__ __attribute__((aligned(16))) float s_scale[kRopeMaxScaleFloats];
+  const int P = a.pos_per_wg;
+  const int64_t b = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * P;  // first token of the work-group
+  const int64_t n_tok = PLANES ? a.len32 : a.len;
+  const int np = (int)(n_tok - t0 < P ? n_tok - t0 : P);
+  const int nrot = (int)(a.len - t0 < np ? (a.len - t0 > 0 ? a.len - t0 : 0) : np);  // tokens with data
+  for (int i = threadIdx.x; i < nrot * H2; i += blockDim.x) {
+    const int64_t src = (a.pos0 + t0 + i / H2) * H2 + i % H2;
+    s_cos[i] = a.rope_cos[src];
+    s_sin[i] = a.rope_sin[src];
+  }
+  const bool staged = a.scale != nullptr && a.scale_rows * D <= kRopeMaxScaleFloats;
+  if (staged)
+    for (int i = threadIdx.x; i < a.scale_rows * D; i += blockDim.x) s_scale[i] = a.scale[i];
+  __syncthreads();
+  const int items = np * a.heads * NP;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int j = it % NP;
+    const int h = (it / NP) % a.heads;
+    const int pl = it / (NP * a.heads);
+    const int64_t tok = t0 + pl;
+    const int64_t bh = b * a.heads + h;
+    if (tok >= a.len) {  // padding key of a scale plane: zero scale bytes for both blocks
+      if (PLANES) {
+        a.scales[(bh * NB + j) * a.len32 + tok] = 0;
+        a.scales[(bh * NB + j + NP) * a.len32 + tok] = 0;
+      }
+      continue;
+    }
+    const int64_t row = bh * a.len + tok;
+    Block32In lo_in, hi_in;
+    load_block32(a.x + row * D + kBlock * j, nullptr, lo_in);
+    load_block32(a.x + row * D + H2 + kBlock * j, nullptr, hi_in);
+    float lo[32], hi[32];
+    unpack_block32(lo_in, lo);
+    unpack_block32(hi_in, hi);
+    const float* cs = s_cos + pl * H2 + kBlock * j;
+    const float* sn = s_sin + pl * H2 + kBlock * j;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      const float x0 = lo[i], x1 = hi[i];
+      const float c = cs[i], s = sn[i];
+      lo[i] = x0 * c - x1 * s;  // RN32 of each product, then of the difference
+      hi[i] = x1 * c + x0 * s;
+    }
+    if (a.scale != nullptr) {
+      const int srow = h / a.heads_per_scale_row;
+      const float* sc = staged ? s_scale + srow * D : a.scale + (int64_t)srow * D;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        lo[i] = lo[i] * sc[kBlock * j + i];
+        hi[i] = hi[i] * sc[H2 + kBlock * j + i];
+      }
+    }
+    uint4 c_lo, c_hi;
+    const uint32_t e_lo = quantize_values32(lo, &c_lo);
+    const uint32_t e_hi = quantize_values32(hi, &c_hi);
+    *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + 16 * j) = c_lo;
+    *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + 16 * (j + NP)) = c_hi;
+    if (PLANES) {
+      a.scales[(bh * NB + j) * a.len32 + tok] = (uint8_t)e_lo;
+      a.scales[(bh * NB + j + NP) * a.len32 + tok] = (uint8_t)e_hi;
+    } else {
+      a.scales[row * NB + j] = (uint8_t)e_lo;
+      a.scales[row * NB + j + NP] = (uint8_t)e_hi;
+    }
+  }
+}
+
+template <int D>
+static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
+  // about one item per thread: positions * heads * (D/64) items per work-group
+  int p = 256 / (a.heads * (D / 64));
+  p = p < 1 ? 1 : (p > kRopeMaxPos ? kRopeMaxPos : p);
+  a.pos_per_wg = p;
+  const int64_t n_tok = a.block_planes ? a.len32 : a.len;
+  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)a.batch);
+  if (a.block_planes) hipLaunchKernelGGL((quantize_rope_kernel<D, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((quantize_rope_kernel<D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return quant_rope_d<64>(a, s);
+    case 128: return quant_rope_d<128>(a, s);
+    case 256: return quant_rope_d<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D>
 static hipError_t quant_rows_d(const QuantRowsArgs& a, hipStream_t s) {
   const int64_t rows = a.block_planes ? a.rows / a.len * a.len32 : a.rows;

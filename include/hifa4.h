@@ -110,6 +110,25 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
                                 void* q_codes, void* q_scales, void* k_codes, void* k_scales,
                                 void* v_codes, void* v_scales, void* hip_stream);
 
+/*
+ * RoPE, Smooth-QK rescale and 4-bit quantization from pre-RoPE inputs, fused (device, async).
+ * [HiFA4 Abstract: Smooth-QK rescales Q and K per channel after RoPE, and at inference only an
+ * element-wise scaling remains, fusible into the preceding step.]  q, k hold FP16 values before
+ * the rotary embedding; rope_cos, rope_sin are FP32 [rope_positions, d/2] device tables of the
+ * rotate-half embedding (entry (p, i) rotates channels i and i + d/2 at position p).  Key t sits
+ * at position t, query r at r + Lk - Lq.  Per pair, in FP32 with one rounding per product and per
+ * sum: y_i = x_i c - x_{i+d/2} s, y_{i+d/2} = x_{i+d/2} c + x_i s; the rotated values are not
+ * rounded to FP16; then Q' = fp32(y * s[g(h)]), K' = fp32(y * inv_s[g]) and the block
+ * quantization of hifa4_quantize_qkv, with the same output layouts.  V is quantized as there.
+ * Errors: those of hifa4_quantize_qkv; HIFA4_ERR_NULL for missing tables when q or k is given;
+ * HIFA4_ERR_SHAPE when rope_positions < Lk or (q given) Lq > Lk.
+ */
+hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, const void* k, const void* v,
+                                     const float* s, const float* inv_s, const float* rope_cos,
+                                     const float* rope_sin, int64_t rope_positions, void* q_codes,
+                                     void* q_scales, void* k_codes, void* k_scales, void* v_codes,
+                                     void* v_scales, void* hip_stream);
+
 /* Number of KV splits hifa4_attention_fwd uses for these dims and options (1 when Lq > 1). */
 int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts);
 

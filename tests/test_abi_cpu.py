@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -109,6 +109,27 @@ def test_quantize_rejects_bad_arguments(L):
     bad = hf.make_dims(1, 4, 2, 80, 64, 64)
     st = L.hifa4_quantize_qkv(ctypes.byref(bad), dummy, None, None, None, None, dummy, dummy, None, None, None, None, None)
     assert st == 3
+
+
+def test_quantize_rope_rejects_bad_arguments(L):
+    dims = hf.make_dims(1, 4, 2, 128, 64, 64)
+    ok = ctypes.c_void_p(256)
+    outs = [ok] * 6
+    # q, k, v, s, inv_s, cos, sin, n_pos, outputs..., stream
+    st = L.hifa4_quantize_qkv_rope(ctypes.byref(dims), ok, ok, None, ok, ok, None, None, 64, *outs, None)
+    assert st == 1 and b"RoPE" in L.hifa4_last_error()
+    st = L.hifa4_quantize_qkv_rope(ctypes.byref(dims), ok, ok, None, ok, ok, ok, ok, 63, *outs, None)
+    assert st == 2 and b"positions" in L.hifa4_last_error()
+    longq = hf.make_dims(1, 4, 2, 128, 65, 64)
+    st = L.hifa4_quantize_qkv_rope(ctypes.byref(longq), ok, ok, None, ok, ok, ok, ok, 64, *outs, None)
+    assert st == 2
+    st = L.hifa4_quantize_qkv_rope(ctypes.byref(dims), ok, ok, None, ok, ok, ctypes.c_void_p(260), ok, 64, *outs,
+                                   None)
+    assert st == 6
+    # V alone needs no tables
+    st = L.hifa4_quantize_qkv_rope(ctypes.byref(dims), None, None, ok, None, None, None, None, 0, None, None, None,
+                                   None, None, None, None)
+    assert st == 1  # v outputs missing, checked before any launch
 
 
 @pytest.mark.parametrize("cfg_id", [0, 1, 3])

@@ -1,0 +1,89 @@
+"""GPU parity of the fused RoPE prologue (hifa4_quantize_qkv_rope) against oracle/rope.py.
+
+Pre-RoPE FP16 inputs and the FP32 RoPE tables go to both sides; every code and scale byte must
+match, and the attention computed from the GPU's codes must match the oracle's attention of the
+oracle's codes (max |d| <= 2e-3 * RMS).  Full size: the batched prefill workload's K and Q,
+compared on sampled (batch, head) slices.
+"""
+import numpy as np
+import pytest
+
+import bit_quantized_flashattention_amd as hf
+from oracle import attention as A
+from oracle import rope
+from oracle import smooth
+import synth
+from gpu_helpers import NAMES, assert_codes_equal, compare_out, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(cfg_id, causal, kv_tile, **over):
+    import torch
+    cfg = synth.config(cfg_id, **over)
+    theta = cfg["rope_theta"] or 1e4
+    q, k, v = synth.make_qkv(cfg, pre_rope=True)
+    qc, kc = synth.make_calibration(cfg)
+    s32, inv32, gate = smooth.calibrate(qc, kc, cfg["alpha"], 4.0)
+    cos32, sin32 = synth.rope_table(theta, cfg["Lk"], cfg["d"])
+    print("case rope", cfg_id, over, flush=True)
+    res = hf.quantize_qkv_rope(to_dev(q), to_dev(k), to_dev(v), to_dev(s32), to_dev(inv32), to_dev(cos32),
+                               to_dev(sin32))
+    qq = rope.quantize_qkv_rope(q, k, v, s32, inv32, cos32, sin32)
+    assert_codes_equal(res, qq)
+    dims = hf.make_dims(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lq"], cfg["Lk"])
+    splits = hf.decode_num_splits(dims, hf.make_opts(causal, 0, kv_tile, 0))
+    out = hf.attention_fwd(res, dims, causal, 0, kv_tile)
+    torch.cuda.synchronize()
+    want = A.attention_p(qq, causal, kv_tile, 0, num_splits=splits if cfg["Lq"] == 1 else 1)
+    compare_out(out.cpu().numpy(), want, "rope-%d" % cfg_id)
+
+
+def test_rope_tiny_noncausal_d64():
+    _case(0, False, 64)
+
+
+def test_rope_qwen_shaped_reduced():
+    _case(1, True, 128, B=2, Hq=8, Hkv=2, Lq=300, Lk=300)
+
+
+def test_rope_ragged_more_keys_than_queries():
+    _case(1, True, 64, B=1, Hq=4, Hkv=1, Lq=77, Lk=333)
+
+
+def test_rope_gemma_shaped_d256():
+    _case(3, True, 128, B=1, Hq=4, Hkv=2, Lq=200, Lk=200)
+
+
+def test_rope_decode_query():
+    _case(1, True, 128, B=3, Hq=8, Hkv=2, Lq=1, Lk=1000)
+
+
+def test_rope_wide_group_two_items_per_thread():
+    # 64 query heads per KV head at d = 256: 512 items per position, one position per
+    # work-group, so each thread serves two items
+    _case(3, False, 128, B=1, Hq=128, Hkv=2, Lq=24, Lk=24)
+
+
+def test_rope_full_size_batched_prefill():
+    import torch
+    cfg = synth.config(2)
+    b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    print("case rope full size config 2", flush=True)
+    q, k, v = synth.make_qkv_device(cfg, pre_rope=True)
+    qc, kc = synth.make_calibration(cfg)
+    s32, inv32, gate = smooth.calibrate(qc, kc, cfg["alpha"], 4.0)
+    cos32, sin32 = synth.rope_table(cfg["rope_theta"], lk, d)
+    res = hf.quantize_qkv_rope(q, k, v, to_dev(s32), to_dev(inv32), to_dev(cos32), to_dev(sin32))
+    torch.cuda.synchronize()
+    group = hq // hkv
+    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
+        g = h // group
+        qh = q[b:b + 1, h:h + 1].cpu().numpy()
+        kh = k[b:b + 1, g:g + 1].cpu().numpy()
+        vh = v[b:b + 1, g:g + 1].cpu().numpy()
+        qq = rope.quantize_qkv_rope(qh, kh, vh, s32[g:g + 1], inv32[g:g + 1], cos32, sin32)
+        for name, want, head in zip(NAMES, qq.packed(), [h, h, g, g, g, g]):
+            got = res[name][b, head].cpu().numpy()
+            bad = np.count_nonzero(got != want[0, 0])
+            assert bad == 0, "(b=%d, head %d) %s: %d bytes differ" % (b, head, name, bad)
