@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
 }
 
 // RoPE (FP32, rotate-half), Smooth-QK and 4-bit quantization of pre-RoPE rows, fused.  A
-// work-group serves pos_per_wg consecutive positions of one batch entry for all H heads, so the
+// work-group serves kRopeMaxPos consecutive positions of one batch entry for all H heads, so the
 // cos/sin rows of those positions (and the Smooth-QK scale table when it is small) are staged in
 // LDS once and shared by every head.  An item is one (position, head, block pair j): channels
 // 32 j .. 32 j + 31 and their rotation partners 32 j + d/2 .. , so each item writes two
@@ -147,11 +147,14 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
   if (staged)
     for (int i = threadIdx.x; i < a.scale_rows * D; i += blockDim.x) s_scale[i] = a.scale[i];
   __syncthreads();
-  const int items = np * a.heads * NP;
+  // items ordered (head, position, block pair): the threads of a wave read consecutive rows of
+  // one head, i.e. one contiguous run of HBM
+  const int items = P * a.heads * NP;
   for (int it = threadIdx.x; it < items; it += blockDim.x) {
     const int j = it % NP;
-    const int h = (it / NP) % a.heads;
-    const int pl = it / (NP * a.heads);
+    const int pl = (it / NP) % P;
+    const int h = it / (NP * P);
+    if (pl >= np) continue;
     const int64_t tok = t0 + pl;
     const int64_t bh = b * a.heads + h;
     if (tok >= a.len) {  // padding key of a scale plane: zero scale bytes for both blocks
@@ -203,9 +206,7 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
 
 template <int D>
 static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
-  // about one item per thread: positions * heads * (D/64) items per work-group
-  int p = 256 / (a.heads * (D / 64));
-  p = p < 1 ? 1 : (p > kRopeMaxPos ? kRopeMaxPos : p);
+  const int p = kRopeMaxPos;
   a.pos_per_wg = p;
   const int64_t n_tok = a.block_planes ? a.len32 : a.len;
   dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)a.batch);
