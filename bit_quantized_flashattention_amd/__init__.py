@@ -58,7 +58,8 @@ def lib():
         L.hifa4_attention_fwd.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 8 + \
             [ctypes.c_size_t, _vp, _vp]
         L.hifa4_attention_fwd.restype = ctypes.c_int
-        L.hifa4_attention_fwd_q16.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 8 + \
+        L.hifa4_attention_fwd_q16.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 4 + \
+            [ctypes.c_int64] + [_vp] * 6 + \
             [ctypes.c_size_t, _vp, _vp]
         L.hifa4_attention_fwd_q16.restype = ctypes.c_int
         L.hifa4_status_string.argtypes = [ctypes.c_int]
@@ -213,9 +214,9 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
                   out=None, workspace=None, tile_stats=None, stream=None, q16=None):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
 
-    ``q16=(q, s)``: take FP16 Q and the Smooth-QK scales (device tensor or None) instead of
-    qkv's Q-hat and quantize Q inside the kernel (hifa4_attention_fwd_q16); qkv then needs only
-    the K-hat and V-hat entries.
+    ``q16=(q, s)`` or ``(q, s, rope_cos, rope_sin)``: take FP16 Q (before RoPE when the tables are
+    given) and the Smooth-QK scales (device tensor or None) instead of qkv's Q-hat and quantize Q
+    inside the kernel (hifa4_attention_fwd_q16); qkv then needs only the K-hat and V-hat entries.
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
@@ -239,9 +240,11 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
             _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
             workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
     else:
-        q, s = q16
+        q, s = q16[0], q16[1]
+        rc, rs = (q16[2], q16[3]) if len(q16) > 2 else (None, None)
+        n_pos = rc.shape[0] if rc is not None else 0
         _check(lib().hifa4_attention_fwd_q16(
-            ctypes.byref(dims), ctypes.byref(opts), _ptr(q), _ptr(s), _ptr(qkv["k_codes"]),
+            ctypes.byref(dims), ctypes.byref(opts), _ptr(q), _ptr(s), _ptr(rc), _ptr(rs), n_pos, _ptr(qkv["k_codes"]),
             _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
             workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
     return (out, stats) if tile_stats is not None else out

@@ -108,7 +108,14 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
       qsc[st] = 127u;
       if (live_col && (D >= 128 || g < 2)) {
         const int c0 = 128 * st + 32 * g;
-        qsc[st] = quantize_block32(qx + c0, a.q_smooth ? a.q_smooth + (int64_t)kvh * D + c0 : nullptr, &qreg[st]);
+        const float* sm = a.q_smooth ? a.q_smooth + (int64_t)kvh * D + c0 : nullptr;
+        if (a.rope_cos != nullptr) {
+          // FP16 query before RoPE, at position Lk - 1
+          qsc[st] = quantize_block32_rope(qx, 4 * st + g, D, a.rope_cos + (lk - 1) * (D / 2),
+                                          a.rope_sin + (lk - 1) * (D / 2), sm, &qreg[st]);
+        } else {
+          qsc[st] = quantize_block32(qx + c0, sm, &qreg[st]);
+        }
       }
     }
   } else {

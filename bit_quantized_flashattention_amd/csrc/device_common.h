@@ -116,6 +116,70 @@ __device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool 
   return quantize_values32(v, codes);
 }
 
+// RoPE (rotate-half, FP32), Smooth-QK and 4-bit quantization of block blk of one FP16 row of
+// width D before RoPE: cos_row and sin_row are the D/2 table entries of the row's position, s
+// the 32 channel scales of the block or nullptr.  A block in the first half takes
+// y = x c - x' s with x' its partner D/2 channels later; a block in the second half takes
+// y = x c + x' s with x' its partner D/2 channels earlier; each product and sum is rounded once.
+// Eight rotated and rescaled values (chunk k of the block); see quantize_block32_rope.
+__device__ __forceinline__ void rope_chunk8(const uint16_t* own, const uint16_t* partner, bool first,
+                                            const float* cos_c, const float* sin_c, const float* s, int k, float* y) {
+  const uint4 xo = *reinterpret_cast<const uint4*>(own + 8 * k);
+  const uint4 xq = *reinterpret_cast<const uint4*>(partner + 8 * k);
+  const float4 ca = *reinterpret_cast<const float4*>(cos_c + 8 * k);
+  const float4 cb = *reinterpret_cast<const float4*>(cos_c + 8 * k + 4);
+  const float4 sa = *reinterpret_cast<const float4*>(sin_c + 8 * k);
+  const float4 sb = *reinterpret_cast<const float4*>(sin_c + 8 * k + 4);
+  const uint32_t wo[4] = {xo.x, xo.y, xo.z, xo.w};
+  const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w};
+  const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+  const float ss[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+  for (int t = 0; t < 8; t++) {
+    const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wo[t / 2] >> 16) : (wo[t / 2] & 0xFFFF)));
+    const float xp = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wq[t / 2] >> 16) : (wq[t / 2] & 0xFFFF)));
+    y[t] = first ? x * cc[t] - xp * ss[t] : x * cc[t] + xp * ss[t];
+  }
+  if (s != nullptr) {
+    const float4 ma = *reinterpret_cast<const float4*>(s + 8 * k);
+    const float4 mb = *reinterpret_cast<const float4*>(s + 8 * k + 4);
+    const float mm[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+#pragma unroll
+    for (int t = 0; t < 8; t++) y[t] = y[t] * mm[t];
+  }
+}
+
+// Two passes of eight values each (the block maximum, then the codes), so only a handful of
+// values are live at a time: it runs in the prologue of kernels with a tight register budget.
+// The empty asm between the passes keeps the second pass from reusing the first pass's loads.
+__device__ __forceinline__ uint32_t quantize_block32_rope(const uint16_t* row, int blk, int D, const float* cos_row,
+                                                          const float* sin_row, const float* s, uint4* codes) {
+  const int half = D / 2;
+  const int c0 = kBlock * blk;
+  const bool first = c0 < half;
+  const int i0 = first ? c0 : c0 - half;  // table column of the block's first channel
+  const uint16_t* own = row + c0;
+  const uint16_t* partner = row + (first ? c0 + half : c0 - half);
+  float amax = 0.0f;
+  for (int k = 0; k < 4; k++) {
+    float y[8];
+    rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y);
+#pragma unroll
+    for (int t = 0; t < 8; t++) amax = fmaxf(amax, fabsf(y[t]));
+  }
+  asm volatile("" ::: "memory");
+  const int e = mx_exponent(amax);
+  const float scale = e8m0_as_float(e);
+  uint32_t w[4];
+  for (int k = 0; k < 4; k++) {
+    float y[8];
+    rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y);
+    w[k] = pack8_fp4(y, scale);
+  }
+  *codes = make_uint4(w[0], w[1], w[2], w[3]);
+  return (uint32_t)(e + 127);
+}
+
 // Both steps for one block (see load_block32 and quantize_loaded32).
 __device__ __forceinline__ uint32_t quantize_block32(const uint16_t* x, const float* s, uint4* codes) {
   Block32In in;

@@ -338,7 +338,8 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
 }
 
 hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
-                                     const float* s, const void* k_codes, const void* k_scales,
+                                     const float* s, const float* rope_cos, const float* rope_sin,
+                                     int64_t rope_positions, const void* k_codes, const void* k_scales,
                                      const void* v_codes, const void* v_scales, void* out, void* workspace,
                                      size_t workspace_bytes, float* tile_stats, void* hip_stream) {
   hifa4_status st = check_dims(dims);
@@ -347,11 +348,19 @@ hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_op
   if (st != HIFA4_OK) return st;
   if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
     return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
-  if (!aligned16({q, s, k_codes, k_scales, v_codes, v_scales, out, workspace, tile_stats}))
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(HIFA4_ERR_NULL, "attention: pass both RoPE tables or neither");
+  if (rope_cos && dims->len_q > dims->len_kv)
+    return fail(HIFA4_ERR_SHAPE, "attention: RoPE positions need len_q <= len_kv (query r sits at r + len_kv - len_q)");
+  if (rope_cos && rope_positions < dims->len_kv)
+    return fail(HIFA4_ERR_SHAPE, "attention: the RoPE tables need at least len_kv positions");
+  if (!aligned16({q, s, rope_cos, rope_sin, k_codes, k_scales, v_codes, v_scales, out, workspace, tile_stats}))
     return fail(HIFA4_ERR_ALIGNMENT, "attention: device pointers must be 16-byte aligned");
   hifa4::AttnArgs a{};
   a.q_fp16 = (const uint16_t*)q;
   a.q_smooth = s;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   a.k_codes = (const uint8_t*)k_codes;
   a.k_scales = (const uint8_t*)k_scales;
   a.v_codes = (const uint8_t*)v_codes;

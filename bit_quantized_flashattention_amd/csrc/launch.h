@@ -35,6 +35,8 @@ struct AttnArgs {
   const uint8_t* q_scales;
   const uint16_t* q_fp16;   // FP16 Q [B, Hq, Lq, d] quantized in the kernel prologue, or nullptr
   const float* q_smooth;    // Smooth-QK scales [Hkv, d] applied to q_fp16, or nullptr
+  const float* rope_cos;    // FP32 [n_pos, d/2]: q_fp16 is before RoPE (query r at r + Lk - Lq), or nullptr
+  const float* rope_sin;
   const uint8_t* k_codes;
   const uint8_t* k_scales;
   const uint8_t* v_codes;

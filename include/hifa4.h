@@ -164,12 +164,16 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
  * Abstract: the Smooth-QK rescale is element-wise and fusible.]  q is FP16 [B, Hq, Lq, d] and s
  * the Smooth-QK scales [Hkv, d] (device, or NULL for no rescale); each work-group rescales and
  * quantizes the query rows it serves exactly as hifa4_quantize_qkv would, in registers, so no
- * Q-hat is written to or read from memory.  The output is bit-identical to hifa4_quantize_qkv
- * (with the same s) followed by hifa4_attention_fwd; every other argument, the workspace rules
- * and the errors are those of hifa4_attention_fwd.
+ * Q-hat is written to or read from memory.  With rope_cos/rope_sin (FP32 [rope_positions, d/2],
+ * both or neither), q is taken before RoPE and rotated first, exactly as hifa4_quantize_qkv_rope
+ * does (query r at position r + Lk - Lq).  The output is bit-identical to hifa4_quantize_qkv (or
+ * hifa4_quantize_qkv_rope) with the same arguments followed by hifa4_attention_fwd; every other
+ * argument, the workspace rules and the errors are those of hifa4_attention_fwd, plus
+ * HIFA4_ERR_SHAPE for tables shorter than Lk or Lq > Lk with RoPE.
  */
 hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
-                                     const float* s, const void* k_codes, const void* k_scales,
+                                     const float* s, const float* rope_cos, const float* rope_sin,
+                                     int64_t rope_positions, const void* k_codes, const void* k_scales,
                                      const void* v_codes, const void* v_scales, void* out, void* workspace,
                                      size_t workspace_bytes, float* tile_stats, void* hip_stream);
 

@@ -49,14 +49,21 @@ def test_misaligned_device_pointers_are_rejected(L):
         args[i] = off
         st = L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(hf.make_opts(causal=True)), *args, None, 0, None, None)
         assert st == 6 and b"aligned" in L.hifa4_last_error(), i
-    for i in range(8):  # fused-Q entry point: q, s, K-hat, V-hat, out, workspace
-        args = [ok] * 8
+    def q16(args, n_pos=64, o=None):
+        # q, s, cos, sin | n_pos | K-hat, V-hat (4), out, workspace
+        return L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(o or hf.make_opts(causal=True)),
+                                         *args[:4], n_pos, *args[4:], 0, None, None)
+    for i in range(10):
+        args = [ok] * 10
         args[i] = off
-        st = L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(hf.make_opts(causal=True)), *args, 0, None, None)
-        assert st == 6, i
-    args = [ok] * 8
+        assert q16(args) == 6, i
+    args = [ok] * 10
     args[0] = None  # q is required; s may be NULL
-    assert L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(hf.make_opts()), *args, 0, None, None) == 1
+    assert q16(args) == 1
+    args = [ok] * 10
+    args[3] = None  # one RoPE table without the other
+    assert q16(args) == 1
+    assert q16([ok] * 10, n_pos=63) == 2  # tables shorter than Lk
     for i in range(11):
         args = [ok] * 11
         args[i] = off

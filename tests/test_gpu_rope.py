@@ -37,6 +37,12 @@ def _case(cfg_id, causal, kv_tile, **over):
     torch.cuda.synchronize()
     want = A.attention_p(qq, causal, kv_tile, 0, num_splits=splits if cfg["Lq"] == 1 else 1)
     compare_out(out.cpu().numpy(), want, "rope-%d" % cfg_id)
+    # the fused-Q entry point rotates the pre-RoPE query in its prologue: bit-identical
+    kv_only = {n: res[n] for n in NAMES[2:]}
+    out16 = hf.attention_fwd(kv_only, dims, causal, 0, kv_tile,
+                             q16=(to_dev(q), to_dev(s32), to_dev(cos32), to_dev(sin32)))
+    torch.cuda.synchronize()
+    assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q RoPE output differs"
 
 
 def test_rope_tiny_noncausal_d64():
