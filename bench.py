@@ -9,7 +9,9 @@ causal prefill (B=8, L=4096, Hq=32/Hkv=8, d=128, P-Reordered normalizer, 128-key
 tiles).  The JSON line also carries the memory-bound split-KV decode (B=64,
 Lk=32768, pre-quantized cache; a step runs split, with the query token quantized
 in-kernel, and merge).  The default warm-up (50 steps, about 40 ms) lets the GPU
-clocks settle before the timed steps.
+clocks settle before the timed steps.  The line also carries the same prefill step from
+pre-RoPE Q and K (rope_prefill: K/V quantized with RoPE by hifa4_quantize_qkv_rope, the query
+quantized in the RoPE quantizer too, then the attention from the codes).
 
     python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
 
@@ -42,6 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-rope", action="store_true", help="skip the pre-RoPE (fused RoPE prologue) variant of the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
     p.add_argument("--workload", default="prefill", choices=["prefill", "prefill-d256", "prefill-L2048"])
@@ -140,6 +143,68 @@ def bench_prefill(args, cfg_id):
     flops = 4.0 * d * pairs * b * hq
     return dict(cfg=cfg, step_ms=step_ms, attn_ms=attn_ms, flops=flops, gate=gate,
                 qkv_inputs=(q, k, v), qkv=qkv, out=out)
+
+
+def bench_rope(args):
+    """The same prefill step from pre-RoPE Q and K: hifa4_quantize_qkv_rope rotates, rescales and
+    quantizes Q and K (and quantizes V) in streaming passes, then the attention from the codes."""
+    import torch
+    import bit_quantized_flashattention_amd as hf
+    import synth
+
+    cfg = synth.config(2)
+    b, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    q, k, v = synth.make_qkv_device(cfg, pre_rope=True)
+    q_cal, k_cal = synth.make_calibration(cfg)
+    s, inv, gate = hf.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
+    sd = torch.from_numpy(s).cuda()
+    invd = torch.from_numpy(inv).cuda()
+    cos32, sin32 = synth.rope_table(cfg["rope_theta"], lk, d)
+    cosd, sind = torch.from_numpy(cos32).cuda(), torch.from_numpy(sin32).cuda()
+    dims = hf.make_dims(b, hq, hkv, d, lq, lk)
+    qkv = hf.quantize_qkv_rope(q, k, v, sd, invd, cosd, sind, dims=dims)
+    out = torch.empty((b, hq, lq, d), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        hf.quantize_qkv_rope(q, k, v, sd, invd, cosd, sind, dims=dims, out=qkv)
+        if ev is not None:
+            ev[1].record(stream)
+        hf.attention_fwd(qkv, dims, cfg["causal"], hf.P_REORDERED, cfg["kv_tile"], out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms = (t1 - t0) * 1e3 / args.steps
+    flops = 4.0 * d * causal_pairs(lq, lk) * b * hq
+    # algorithmic bytes of the Q, K (RoPE) and V quantizers: FP16 in, codes and scales out, the
+    # tables and the Smooth-QK scales once
+    elems = b * (hq + 2 * hkv) * lk * d
+    q_bytes = elems * 2 + elems // 2 + elems // 32 + lk * d * 4 + 2 * hkv * d * 4
+    res = {
+        "workload": "%s from pre-RoPE Q/K: Q/K/V quantize with RoPE on Q and K, then attention" % cfg["name"],
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(step_ms, 4),
+        "attention_ms": round(attn_ms, 4),
+        "quantize_qkv_rope": {"us": round(quant_ms * 1e3, 1), "bytes": q_bytes,
+                             "achieved_gbs": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS},
+    }
+    del q, k, v, qkv, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(args):
@@ -280,6 +345,8 @@ def main():
         line["cpu_baseline"] = cpu_baseline(args, pre)
     del pre
     torch.cuda.empty_cache()
+    if not args.no_rope and args.workload == "prefill":
+        line["rope_prefill"] = bench_rope(args)
     if not args.no_decode:
         line["decode"] = bench_decode(args)
     if args.traffic_probe:

@@ -246,25 +246,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   const bool fused_q = a.q_fp16 != nullptr;
   const bool q_has = q0 + col < lq && (D >= 128 || g < 2);
   Block32In qin[KSTEPS];
-  if (fused_q && a.rope_cos != nullptr) {
-    // FP16 Q before RoPE: each lane rotates its block with the partner block, then rescales and
-    // quantizes.  This runs first, before the tile-loop state exists, so its registers are free.
-    const int q = q0 + col;
-    const int64_t pos = (int64_t)q + lk - lq;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; s++) {
-      qreg[s] = make_uint4(0u, 0u, 0u, 0u);
-      qsc[s] = 127u;
-      if (q_has)
-        qsc[s] = quantize_block32_rope(a.q_fp16 + (((int64_t)b * a.heads_q + h) * lq + q) * D, 4 * s + g, D,
-                                       a.rope_cos + pos * (D / 2), a.rope_sin + pos * (D / 2),
-                                       q_smooth_blk(a, kvh, D, 128 * s + 32 * g), &qreg[s]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
   {
     const int q = q0 + col;
-    if (fused_q && a.rope_cos == nullptr) {
+    if (fused_q) {
       if (q_has) {
         const uint16_t* qx = a.q_fp16 + (((int64_t)b * a.heads_q + h) * lq + q) * D;
         // the channel scales are loaded with the values where registers allow (one K-step)
@@ -272,7 +256,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
         for (int s = 0; s < KSTEPS; s++)
           load_block32(qx + 128 * s + 32 * g, KSTEPS == 1 ? q_smooth_blk(a, kvh, D, 128 * s + 32 * g) : nullptr, qin[s]);
       }
-    } else if (!fused_q) {  // Q-hat from memory (the RoPE branch above has filled qreg already)
+    } else {
       const uint8_t* qc = a.q_codes + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / 2);
       const uint8_t* qs = a.q_scales + ((int64_t)b * a.heads_q + h) * (int64_t)lq * (D / kBlock);
 #pragma unroll
@@ -335,7 +319,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
 #pragma unroll
   for (int p = 0; p < kStages - 1; p++)
     if (p < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
-  if (fused_q && a.rope_cos == nullptr) {
+  if (fused_q) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KSTEPS; s++) {

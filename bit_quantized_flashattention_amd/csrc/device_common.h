@@ -149,9 +149,7 @@ __device__ __forceinline__ void rope_chunk8(const uint16_t* own, const uint16_t*
   }
 }
 
-// Two passes of eight values each (the block maximum, then the codes), so only a handful of
-// values are live at a time: it runs in the prologue of kernels with a tight register budget.
-// The empty asm between the passes keeps the second pass from reusing the first pass's loads.
+// One pass over four chunks of eight values; the 32 results stay live for the block maximum.
 __device__ __forceinline__ uint32_t quantize_block32_rope(const uint16_t* row, int blk, int D, const float* cos_row,
                                                           const float* sin_row, const float* s, uint4* codes) {
   const int half = D / 2;
@@ -160,24 +158,10 @@ __device__ __forceinline__ uint32_t quantize_block32_rope(const uint16_t* row, i
   const int i0 = first ? c0 : c0 - half;  // table column of the block's first channel
   const uint16_t* own = row + c0;
   const uint16_t* partner = row + (first ? c0 + half : c0 - half);
-  float amax = 0.0f;
-  for (int k = 0; k < 4; k++) {
-    float y[8];
-    rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y);
+  float y[32];
 #pragma unroll
-    for (int t = 0; t < 8; t++) amax = fmaxf(amax, fabsf(y[t]));
-  }
-  asm volatile("" ::: "memory");
-  const int e = mx_exponent(amax);
-  const float scale = e8m0_as_float(e);
-  uint32_t w[4];
-  for (int k = 0; k < 4; k++) {
-    float y[8];
-    rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y);
-    w[k] = pack8_fp4(y, scale);
-  }
-  *codes = make_uint4(w[0], w[1], w[2], w[3]);
-  return (uint32_t)(e + 127);
+  for (int k = 0; k < 4; k++) rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y + 8 * k);
+  return quantize_values32(y, codes);
 }
 
 // Both steps for one block (see load_block32 and quantize_loaded32).
@@ -289,10 +273,9 @@ __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, 
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    // every byte of x is written by one of the four conversions below, so it needs no initial
-    // value (an empty asm hands over whatever the register holds, instead of a move of 0)
-    uint32_t x;
-    asm volatile("" : "=v"(x));
+    // every byte of x is written by one of the four conversions below, so its initial value does
+    // not matter: the first conversion writes into the probabilities' own register (no move of 0)
+    uint32_t x = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int k = 8 * q + 2 * j;  // key offsets k, k + 1
@@ -300,7 +283,7 @@ __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, 
       const float u1 = keep_f32(__builtin_fmaf(s[s_index(k + 1)], C, nbm));
       const uint32_t pr = exp2_h2(pack_h2(u0, u1));
       p16[k / 2] = pr;
-      if (j == 0) x = cvt_fp4x2_h<0>(x, pr);
+      if (j == 0) x = cvt_fp4x2_h<0>(pr, pr);
       if (j == 1) x = cvt_fp4x2_h<1>(x, pr);
       if (j == 2) x = cvt_fp4x2_h<2>(x, pr);
       if (j == 3) x = cvt_fp4x2_h<3>(x, pr);

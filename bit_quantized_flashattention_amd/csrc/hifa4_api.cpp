@@ -350,8 +350,9 @@ hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_op
     return fail(HIFA4_ERR_NULL, "attention: a tensor pointer is NULL");
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(HIFA4_ERR_NULL, "attention: pass both RoPE tables or neither");
-  if (rope_cos && dims->len_q > dims->len_kv)
-    return fail(HIFA4_ERR_SHAPE, "attention: RoPE positions need len_q <= len_kv (query r sits at r + len_kv - len_q)");
+  if (rope_cos && dims->len_q != 1)
+    return fail(HIFA4_ERR_UNSUPPORTED, "attention: in-kernel RoPE is for decode (len_q == 1); for prefill use "
+                                       "hifa4_quantize_qkv_rope, then hifa4_attention_fwd");
   if (rope_cos && rope_positions < dims->len_kv)
     return fail(HIFA4_ERR_SHAPE, "attention: the RoPE tables need at least len_kv positions");
   if (!aligned16({q, s, rope_cos, rope_sin, k_codes, k_scales, v_codes, v_scales, out, workspace, tile_stats}))

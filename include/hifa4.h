@@ -164,12 +164,14 @@ hifa4_status hifa4_attention_fwd(const hifa4_dims* dims, const hifa4_attn_opts* 
  * Abstract: the Smooth-QK rescale is element-wise and fusible.]  q is FP16 [B, Hq, Lq, d] and s
  * the Smooth-QK scales [Hkv, d] (device, or NULL for no rescale); each work-group rescales and
  * quantizes the query rows it serves exactly as hifa4_quantize_qkv would, in registers, so no
- * Q-hat is written to or read from memory.  With rope_cos/rope_sin (FP32 [rope_positions, d/2],
- * both or neither), q is taken before RoPE and rotated first, exactly as hifa4_quantize_qkv_rope
- * does (query r at position r + Lk - Lq).  The output is bit-identical to hifa4_quantize_qkv (or
- * hifa4_quantize_qkv_rope) with the same arguments followed by hifa4_attention_fwd; every other
- * argument, the workspace rules and the errors are those of hifa4_attention_fwd, plus
- * HIFA4_ERR_SHAPE for tables shorter than Lk or Lq > Lk with RoPE.
+ * Q-hat is written to or read from memory.  Decode (Lq == 1) also takes rope_cos/rope_sin
+ * (FP32 [rope_positions, d/2], both or neither): q is then taken before RoPE and rotated first,
+ * exactly as hifa4_quantize_qkv_rope does (the query at position Lk - 1).  The output is
+ * bit-identical to hifa4_quantize_qkv (or hifa4_quantize_qkv_rope) with the same arguments
+ * followed by hifa4_attention_fwd; every other argument, the workspace rules and the errors are
+ * those of hifa4_attention_fwd, plus HIFA4_ERR_SHAPE for tables shorter than Lk and
+ * HIFA4_ERR_UNSUPPORTED for RoPE tables with Lq > 1 (prefill rotates Q faster as a streaming
+ * pass: hifa4_quantize_qkv_rope, then hifa4_attention_fwd).
  */
 hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
                                      const float* s, const float* rope_cos, const float* rope_sin,

@@ -49,9 +49,11 @@ def test_misaligned_device_pointers_are_rejected(L):
         args[i] = off
         st = L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(hf.make_opts(causal=True)), *args, None, 0, None, None)
         assert st == 6 and b"aligned" in L.hifa4_last_error(), i
-    def q16(args, n_pos=64, o=None):
+    dec = hf.make_dims(1, 4, 2, 128, 1, 64)  # in-kernel RoPE is a decode feature
+
+    def q16(args, n_pos=64, dm=dec):
         # q, s, cos, sin | n_pos | K-hat, V-hat (4), out, workspace
-        return L.hifa4_attention_fwd_q16(ctypes.byref(dims), ctypes.byref(o or hf.make_opts(causal=True)),
+        return L.hifa4_attention_fwd_q16(ctypes.byref(dm), ctypes.byref(hf.make_opts(causal=True)),
                                          *args[:4], n_pos, *args[4:], 0, None, None)
     for i in range(10):
         args = [ok] * 10
@@ -64,6 +66,7 @@ def test_misaligned_device_pointers_are_rejected(L):
     args[3] = None  # one RoPE table without the other
     assert q16(args) == 1
     assert q16([ok] * 10, n_pos=63) == 2  # tables shorter than Lk
+    assert q16([ok] * 10, dm=dims) == 3  # RoPE tables with a prefill shape
     for i in range(11):
         args = [ok] * 11
         args[i] = off

@@ -37,12 +37,17 @@ def _case(cfg_id, causal, kv_tile, **over):
     torch.cuda.synchronize()
     want = A.attention_p(qq, causal, kv_tile, 0, num_splits=splits if cfg["Lq"] == 1 else 1)
     compare_out(out.cpu().numpy(), want, "rope-%d" % cfg_id)
-    # the fused-Q entry point rotates the pre-RoPE query in its prologue: bit-identical
+    # decode: the fused-Q entry point rotates the pre-RoPE query in its prologue, bit-identically;
+    # prefill refuses the tables (the streaming RoPE quantizer is the faster route there)
     kv_only = {n: res[n] for n in NAMES[2:]}
-    out16 = hf.attention_fwd(kv_only, dims, causal, 0, kv_tile,
-                             q16=(to_dev(q), to_dev(s32), to_dev(cos32), to_dev(sin32)))
-    torch.cuda.synchronize()
-    assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q RoPE output differs"
+    q16 = (to_dev(q), to_dev(s32), to_dev(cos32), to_dev(sin32))
+    if cfg["Lq"] == 1:
+        out16 = hf.attention_fwd(kv_only, dims, causal, 0, kv_tile, q16=q16)
+        torch.cuda.synchronize()
+        assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q RoPE output differs"
+    else:
+        with pytest.raises(hf.Hifa4Error):
+            hf.attention_fwd(kv_only, dims, causal, 0, kv_tile, q16=q16)
 
 
 def test_rope_tiny_noncausal_d64():
@@ -63,6 +68,11 @@ def test_rope_gemma_shaped_d256():
 
 def test_rope_decode_query():
     _case(1, True, 128, B=3, Hq=8, Hkv=2, Lq=1, Lk=1000)
+
+
+def test_rope_decode_d64_and_d256():
+    _case(0, True, 64, B=2, Hq=4, Hkv=2, Lq=1, Lk=200)
+    _case(3, True, 128, B=2, Hq=8, Hkv=2, Lq=1, Lk=300)
 
 
 def test_rope_wide_group_two_items_per_thread():
