@@ -30,7 +30,7 @@ class Dims(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("normalizer", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64)]
 
 
 _lib = None
@@ -51,6 +51,8 @@ def lib():
         L.hifa4_quantize_qkv.restype = ctypes.c_int
         L.hifa4_quantize_qkv_rope.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 7 + [ctypes.c_int64] + [_vp] * 7
         L.hifa4_quantize_qkv_rope.restype = ctypes.c_int
+        L.hifa4_cache_append.argtypes = [ctypes.POINTER(Dims), ctypes.c_int64] + [_vp] * 5 + [ctypes.c_int64] + [_vp] * 6
+        L.hifa4_cache_append.restype = ctypes.c_int
         L.hifa4_decode_num_splits.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)]
         L.hifa4_decode_num_splits.restype = ctypes.c_int32
         L.hifa4_attention_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)]
@@ -85,8 +87,8 @@ def make_dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
     return Dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv)
 
 
-def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0):
-    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits))
+def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0):
+    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity))
 
 
 def _ptr(t):
@@ -195,6 +197,47 @@ def quantize_qkv_rope(q=None, k=None, v=None, s=None, inv_s=None, rope_cos=None,
     return res
 
 
+def cache_shapes(batch, heads_kv, head_dim, capacity):
+    """Shapes of the 4-bit K-hat / V-hat cache buffers of hifa4_cache_append (and of the stage)."""
+    c32 = -(-capacity // 32) * 32
+    return {
+        "k_codes": (batch, heads_kv, capacity, head_dim // 2),
+        "k_scales": (batch, heads_kv, head_dim // 32, c32),
+        "v_codes": (batch, heads_kv, c32 // 32, head_dim, 16),
+        "v_scales": (batch, heads_kv, c32 // 32, head_dim),
+        "v_stage": (batch, heads_kv, 32, head_dim),
+    }
+
+
+def make_cache(batch, heads_kv, head_dim, capacity, device="cuda"):
+    """Empty cache buffers (dict) for cache_append / attention_fwd(kv_capacity=...)."""
+    import torch
+    out = {}
+    for name, shp in cache_shapes(batch, heads_kv, head_dim, capacity).items():
+        dt = torch.float16 if name == "v_stage" else torch.uint8
+        out[name] = torch.zeros(shp, dtype=dt, device=device)
+    out["capacity"] = capacity
+    out["length"] = 0
+    return out
+
+
+def cache_append(cache, k_new, v_new, inv_s=None, rope_cos=None, rope_sin=None, heads_q=None, stream=None):
+    """Append k_new, v_new (CUDA float16 [B, Hkv, n, d]) to ``cache``; returns the new length."""
+    import torch
+    b, hkv, n, d = k_new.shape
+    for t in (k_new, v_new):
+        if not t.is_cuda or t.dtype != torch.float16 or not t.is_contiguous():
+            raise ValueError("k_new, v_new must be contiguous CUDA float16 tensors")
+    dims = make_dims(b, heads_q or hkv, hkv, d, n, cache["length"])
+    n_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    _check(lib().hifa4_cache_append(
+        ctypes.byref(dims), cache["capacity"], _ptr(k_new), _ptr(v_new), _ptr(inv_s), _ptr(rope_cos), _ptr(rope_sin),
+        n_pos, _ptr(cache["k_codes"]), _ptr(cache["k_scales"]), _ptr(cache["v_codes"]), _ptr(cache["v_scales"]),
+        _ptr(cache["v_stage"]), _stream(stream)))
+    cache["length"] += n
+    return cache["length"]
+
+
 def decode_num_splits(dims, opts):
     return int(lib().hifa4_decode_num_splits(ctypes.byref(dims), ctypes.byref(opts)))
 
@@ -211,18 +254,20 @@ def stats_shape(dims, kv_tile):
 
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
-                  out=None, workspace=None, tile_stats=None, stream=None, q16=None):
+                  out=None, workspace=None, tile_stats=None, stream=None, q16=None, kv_capacity=0):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
 
     ``q16=(q, s)`` or ``(q, s, rope_cos, rope_sin)``: take FP16 Q (before RoPE when the tables are
     given) and the Smooth-QK scales (device tensor or None) instead of qkv's Q-hat and quantize Q
     inside the kernel (hifa4_attention_fwd_q16); qkv then needs only the K-hat and V-hat entries.
+    ``kv_capacity``: the key rows allocated per (batch, KV head) when qkv's K-hat / V-hat live in a
+    cache (make_cache / cache_append); 0 = Lk.
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
     """
     import torch
-    opts = make_opts(causal, normalizer, kv_tile, num_splits)
+    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity)
     dev = qkv["k_codes"].device
     if out is None:
         out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16, device=dev)

@@ -27,7 +27,7 @@ struct TileOps {
 template <int D>
 __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, const uint8_t* ks,
                                           const uint8_t* vc, const uint8_t* vs, int64_t k0,
-                                          int64_t lk, int64_t lk32, int bc, int col, int g) {
+                                          int64_t lk, int64_t lk32, int64_t plane, int bc, int col, int g) {
   constexpr int KSTEPS = TileOps<D>::KSTEPS;
   constexpr int CB = TileOps<D>::CB;
   const bool lane_k = D >= 128 || g < 2;
@@ -44,7 +44,7 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
   const int64_t kfirst = k0 + 32 * (col >> 2) + 8 * (col & 3);
 #pragma unroll
   for (int st = 0; st < KSTEPS; st++)
-    t.ksc[st] = (kfirst < lk32 && lane_k) ? *reinterpret_cast<const uint2*>(ks + (int64_t)(4 * st + g) * lk32 + kfirst)
+    t.ksc[st] = (kfirst < lk32 && lane_k) ? *reinterpret_cast<const uint2*>(ks + (int64_t)(4 * st + g) * plane + kfirst)
                                           : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   const bool okv = 32 * g < bc && k0 + 32 * g < lk32;
   const int64_t row = (k0 / kBlock + g) * D;  // block-major V-hat: cells (32-key block, channel)
@@ -88,13 +88,15 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   int t_hi = t_lo + a.tiles_per_split;
   if (t_hi > a.n_tiles) t_hi = a.n_tiles;
 
-  const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * lk * (D / 2);
-  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * lk32 * (D / kBlock);
-  const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / 2);
-  const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (lk32 / kBlock);
+  // slices start at the buffers' strides (the rows allocated per (batch, KV head))
+  const int64_t rows = a.kv_rows, rows32 = a.kv_rows32;
+  const uint8_t* kc = a.k_codes + ((int64_t)b * a.heads_kv + kvh) * rows * (D / 2);
+  const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * rows32 * (D / kBlock);
+  const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (rows32 / 2);
+  const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (rows32 / kBlock);
   // the first tile is put in flight before the query is loaded, so the two latencies overlap
   TileOps<D> cur, nxt;
-  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, bc, col, g);
+  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, rows32, bc, col, g);
 
   // Q-hat^T operand: column = query head, K-chunk g
   uint4 qreg[KSTEPS];
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
 
   for (int tile = t_lo; tile < t_hi; tile++) {
     const int64_t k0 = (int64_t)tile * bc;
-    if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, k0 + bc, lk, lk32, bc, col, g);
+    if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, k0 + bc, lk, lk32, rows32, bc, col, g);
     float s[32];
 #pragma unroll
     for (int tt = 0; tt < 8; tt++) {

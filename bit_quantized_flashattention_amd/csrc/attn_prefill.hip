@@ -94,7 +94,7 @@ struct LoadOp {
 };
 
 template <int D>
-__device__ __forceinline__ LoadOp load_op(int i, int lane, int lk32) {
+__device__ __forceinline__ LoadOp load_op(int i, int lane, int plane) {
   using C = Cfg<D>;
   LoadOp op;
   const int g = lane >> 4, col = lane & 15;
@@ -115,7 +115,7 @@ __device__ __forceinline__ LoadOp load_op(int i, int lane, int lk32) {
     const int pos = q * 256 + 4 * lane;  // [block][key] rows of 128 bytes
     op.sec = 2;
     op.lds = C::kKS + q * 256;
-    op.voff = (pos / kTileKeys) * lk32 + pos % kTileKeys;
+    op.voff = (pos / kTileKeys) * plane + pos % kTileKeys;  // plane: K-hat scale plane stride
   } else {
     const int q = i - C::kKCInstr - C::kVCInstr - C::kKSInstr;
     op.sec = 3;
@@ -233,6 +233,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   // heaviest causal blocks first: they start while the short ones fill the tail
   const int qblk = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   const int lq = (int)a.len_q, lk = (int)a.len_kv, lk32 = (int)a.len_kv32;
+  const int64_t rows = a.kv_rows, rows32 = a.kv_rows32;  // strides of the K-hat / V-hat buffers
   const int q_wg = qblk * bq;
   const int q0 = q_wg + 16 * (wave % wph);  // first query row of this wave
   const int shift = lk - lq;                // causal: key c visible to query r iff c <= r + shift
@@ -296,17 +297,19 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
 
   const int64_t slice = (int64_t)b * a.heads_kv + kvh;
   Slices sl;
-  sl.r[0] = make_desc(a.k_codes + slice * lk * (D / 2), (int64_t)lk * (D / 2));
-  sl.r[1] = make_desc(a.v_codes + slice * lk32 * (D / 2), (int64_t)lk32 * (D / 2));
-  sl.r[2] = make_desc(a.k_scales + slice * (D / kBlock) * lk32, (int64_t)(D / kBlock) * lk32);
-  sl.r[3] = make_desc(a.v_scales + slice * (lk32 / kBlock) * D, (int64_t)(lk32 / kBlock) * D);
+  // slices start at the buffers' strides; the ranges cover the attended keys only, so loads past
+  // them return zeros
+  sl.r[0] = make_desc(a.k_codes + slice * rows * (D / 2), (int64_t)lk * (D / 2));
+  sl.r[1] = make_desc(a.v_codes + slice * rows32 * (D / 2), (int64_t)lk32 * (D / 2));
+  sl.r[2] = make_desc(a.k_scales + slice * (D / kBlock) * rows32, (int64_t)(D / kBlock) * rows32);
+  sl.r[3] = make_desc(a.v_scales + slice * (rows32 / kBlock) * D, (int64_t)(lk32 / kBlock) * D);
   const uint32_t smem_lds = lds_addr(smem);
   // this wave's share of the stage loads: instructions wave, wave + W, ...
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n_loads = wave_u < Cf::kInstr ? (Cf::kInstr - wave_u + W - 1) / W : 0;
   LoadOp ops[Cf::kMaxLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < Cf::kMaxLoadsPerWave; i++) ops[i] = load_op<D>(wave_u + W * i, lane, lk32);
+  for (int i = 0; i < Cf::kMaxLoadsPerWave; i++) ops[i] = load_op<D>(wave_u + W * i, lane, (int)rows32);
   const float C = a.c_log2;
 
   // per-lane LDS offsets of this lane's MFMA operands (see the reads in the tile loop)

@@ -89,6 +89,8 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
   if (o->kv_tile != 64 && o->kv_tile != 128) return fail(HIFA4_ERR_UNSUPPORTED, "kv_tile must be 64 or 128");
   if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
+  if (o->kv_capacity != 0 && (o->kv_capacity < d->len_kv || o->kv_capacity > (int64_t(1) << 31)))
+    return fail(HIFA4_ERR_SHAPE, "kv_capacity must be 0 or in [len_kv, 2^31]");
   return HIFA4_OK;
 }
 
@@ -254,6 +256,47 @@ hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, cons
   return ok();
 }
 
+hifa4_status hifa4_cache_append(const hifa4_dims* dims, int64_t kv_capacity, const void* k_new, const void* v_new,
+                                const float* inv_s, const float* rope_cos, const float* rope_sin,
+                                int64_t rope_positions, void* k_codes, void* k_scales, void* v_codes,
+                                void* v_scales, void* v_stage, void* hip_stream) {
+  if (dims == nullptr) return fail(HIFA4_ERR_NULL, "dims is NULL");
+  if (dims->batch < 1 || dims->heads_kv < 1 || dims->len_q < 1 || dims->len_kv < 0)
+    return fail(HIFA4_ERR_SHAPE, "append: need batch, heads_kv, len_q (new keys) >= 1 and len_kv >= 0");
+  if (dims->head_dim != 64 && dims->head_dim != 128 && dims->head_dim != 256)
+    return fail(HIFA4_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (dims->len_kv + dims->len_q > kv_capacity || kv_capacity > (int64_t(1) << 31))
+    return fail(HIFA4_ERR_SHAPE, "append: len_kv + len_q must not exceed kv_capacity (<= 2^31)");
+  if (!k_new || !v_new || !k_codes || !k_scales || !v_codes || !v_scales || !v_stage)
+    return fail(HIFA4_ERR_NULL, "append: a tensor pointer is NULL");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(HIFA4_ERR_NULL, "append: pass both RoPE tables or neither");
+  if (rope_cos && rope_positions < dims->len_kv + dims->len_q)
+    return fail(HIFA4_ERR_SHAPE, "append: the RoPE tables need len_kv + len_q positions");
+  if (!aligned16({k_new, v_new, inv_s, rope_cos, rope_sin, k_codes, k_scales, v_codes, v_scales, v_stage}))
+    return fail(HIFA4_ERR_ALIGNMENT, "append: device pointers must be 16-byte aligned");
+  hifa4::CacheAppendArgs a{};
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.inv_s = inv_s;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.bh = (int64_t)dims->batch * dims->heads_kv;
+  a.heads_kv = dims->heads_kv;
+  a.d = dims->head_dim;
+  a.len0 = dims->len_kv;
+  a.n = dims->len_q;
+  a.rows = kv_capacity;
+  a.rows32 = round32(kv_capacity);
+  a.k_codes = (uint8_t*)k_codes;
+  a.k_scales = (uint8_t*)k_scales;
+  a.v_codes = (uint8_t*)v_codes;
+  a.v_scales = (uint8_t*)v_scales;
+  a.v_stage = (uint16_t*)v_stage;
+  hipError_t e = hifa4::launch_cache_append(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("append: ") + hipGetErrorString(e));
+  return ok();
+}
+
 int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts) {
   if (check_dims(dims) != HIFA4_OK || check_opts(dims, opts) != HIFA4_OK) return 0;
   return resolve_splits(dims, opts);
@@ -281,6 +324,8 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
   a.len_q = dims->len_q;
   a.len_kv = dims->len_kv;
   a.len_kv32 = round32(dims->len_kv);
+  a.kv_rows = opts->kv_capacity ? opts->kv_capacity : dims->len_kv;
+  a.kv_rows32 = round32(a.kv_rows);
   a.kv_tile = opts->kv_tile;
   a.n_tiles = (int32_t)((dims->len_kv + opts->kv_tile - 1) / opts->kv_tile);
   a.causal = opts->causal;

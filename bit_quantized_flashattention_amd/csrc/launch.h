@@ -47,6 +47,7 @@ struct AttnArgs {
   uint16_t* part_ml;    // decode: FP16 [B*Hq*S, 2] (m, l)
   int32_t batch, heads_q, heads_kv, d;
   int64_t len_q, len_kv, len_kv32;
+  int64_t kv_rows, kv_rows32;  // key rows allocated per (batch, KV head): the buffers' strides
   int32_t kv_tile;      // keys per tile (64 or 128)
   int32_t n_tiles;      // ceil(Lk / kv_tile)
   int32_t causal;
@@ -75,7 +76,26 @@ struct QuantRopeArgs {
   uint8_t* codes;       // [B*H*len, d/2]
   uint8_t* scales;
 };
+struct CacheAppendArgs {
+  const uint16_t* k_new;  // FP16 [B*Hkv, n, d] (before RoPE when rope_cos is set)
+  const uint16_t* v_new;  // FP16 [B*Hkv, n, d]
+  const float* inv_s;     // Smooth-QK K factors [Hkv, d] or nullptr
+  const float* rope_cos;  // FP32 [n_pos, d/2] or nullptr
+  const float* rope_sin;
+  int64_t bh;             // B * Hkv
+  int32_t heads_kv;
+  int32_t d;
+  int64_t len0;           // keys already in the cache
+  int64_t n;              // keys appended
+  int64_t rows, rows32;   // capacity per (batch, KV head), and rounded up to 32
+  uint8_t* k_codes;       // [B*Hkv, rows, d/2]
+  uint8_t* k_scales;      // [B*Hkv, d/32, rows32]
+  uint8_t* v_codes;       // [B*Hkv, rows32/32, d, 16]
+  uint8_t* v_scales;      // [B*Hkv, rows32/32, d]
+  uint16_t* v_stage;      // FP16 [B*Hkv, 32, d]: the keys of the open V-hat block
+};
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
 hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s);
 hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);

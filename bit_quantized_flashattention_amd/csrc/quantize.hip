@@ -224,6 +224,74 @@ hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s) {
   }
 }
 
+// Append n keys to a 4-bit cache, one work-group per (batch, KV head).  K-hat rows are
+// independent: each new key is rotated (optional), rescaled and quantized into its row and its
+// scale-plane column.  V-hat blocks run along keys, so every block the new keys touch is
+// quantized again from FP16: keys before len0 come from the stage (the FP16 keys of the block
+// that was still open), new keys from v_new, and positions past len0 + n are zero, exactly as
+// the whole-sequence quantizer pads the last block.  The stage then receives the keys of the
+// block left open, after every read of the old stage has happened (one barrier).
+template <int D>
+__global__ __launch_bounds__(256) void cache_append_kernel(CacheAppendArgs a) {
+  constexpr int NB = D / kBlock;
+  const int64_t bh = blockIdx.x;
+  const int h = (int)(bh % a.heads_kv);
+  const int64_t end = a.len0 + a.n;
+  // K-hat: one thread per (new key, 32-channel block)
+  for (int64_t it = threadIdx.x; it < a.n * NB; it += blockDim.x) {
+    const int blk = (int)(it % NB);
+    const int64_t t = it / NB, pos = a.len0 + t;
+    const uint16_t* x = a.k_new + (bh * a.n + t) * D;
+    const float* sc = a.inv_s ? a.inv_s + (int64_t)h * D + kBlock * blk : nullptr;
+    uint4 out;
+    const uint32_t e8 = a.rope_cos ? quantize_block32_rope(x, blk, D, a.rope_cos + pos * (D / 2),
+                                                           a.rope_sin + pos * (D / 2), sc, &out)
+                                   : quantize_block32(x + kBlock * blk, sc, &out);
+    *reinterpret_cast<uint4*>(a.k_codes + (bh * a.rows + pos) * (D / 2) + 16 * blk) = out;
+    a.k_scales[(bh * NB + blk) * a.rows32 + pos] = (uint8_t)e8;
+  }
+  // V-hat: every touched 32-key block, one thread per channel
+  const int64_t open0 = a.len0 - a.len0 % kBlock;  // first key of the block that was open
+  for (int64_t jb = a.len0 / kBlock; jb * kBlock < end; jb++) {
+    for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        const int64_t p = jb * kBlock + i;
+        uint16_t bits = 0;
+        if (p < a.len0) bits = a.v_stage[(bh * kBlock + (p - open0)) * D + ch];
+        else if (p < end) bits = a.v_new[(bh * a.n + (p - a.len0)) * D + ch];
+        v[i] = (float)__builtin_bit_cast(_Float16, bits);
+      }
+      uint4 out;
+      const uint32_t e8 = quantize_values32(v, &out);
+      const int64_t blk_row = (bh * (a.rows32 / kBlock) + jb) * D;
+      *reinterpret_cast<uint4*>(a.v_codes + (blk_row + ch) * 16) = out;
+      a.v_scales[blk_row + (D / 16) * (ch % 16) + ch / 16] = (uint8_t)e8;
+    }
+  }
+  __syncthreads();
+  // the block left open: its keys (FP16) go to the stage for the next append
+  const int64_t open1 = end - end % kBlock;
+  for (int64_t it = threadIdx.x; it < (end - open1) * D; it += blockDim.x) {
+    const int64_t p = open1 + it / D;
+    const int ch = (int)(it % D);
+    if (p >= a.len0)  // keys before len0 are in the stage already, in the same slot
+      a.v_stage[(bh * kBlock + (p - open1)) * D + ch] = a.v_new[(bh * a.n + (p - a.len0)) * D + ch];
+  }
+}
+
+hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t s) {
+  const dim3 grid((uint32_t)a.bh);
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL(cache_append_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(cache_append_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(cache_append_kernel<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t quant_rows_d(const QuantRowsArgs& a, hipStream_t s) {
   const int64_t rows = a.block_planes ? a.rows / a.len * a.len32 : a.rows;

@@ -78,6 +78,10 @@ typedef struct {
                          state is rounded once per tile) */
   int32_t num_splits; /* Lq == 1 only: split-KV count; 0 = choose automatically (see
                          hifa4_decode_num_splits); part of the numerical definition */
+  int64_t kv_capacity; /* key rows allocated per (batch, KV head) in the K-hat / V-hat buffers
+                          (a cache filled by hifa4_cache_append); 0 = Lk.  The layouts above then
+                          hold with Lk (Lk32) replaced by kv_capacity (rounded up to 32) for the
+                          strides, while Lk keys are attended */
 } hifa4_attn_opts;
 
 /*
@@ -128,6 +132,28 @@ hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, cons
                                      const float* rope_sin, int64_t rope_positions, void* q_codes,
                                      void* q_scales, void* k_codes, void* k_scales, void* v_codes,
                                      void* v_scales, void* hip_stream);
+
+/*
+ * Append keys to a 4-bit K-hat / V-hat cache (device, async).  The step after prefill in decoding
+ * (the pages' decode workload reads a pre-quantized cache).  dims->len_kv = keys already in the
+ * cache (L0), dims->len_q = keys appended (n >= 1); heads_q is not used.  The cache buffers use
+ * the layouts above with Lk replaced by kv_capacity (C >= L0 + n) for the strides:
+ *   k_codes [B, Hkv, C, d/2], k_scales [B, Hkv, d/32, C32], v_codes [B, Hkv, C32/32, d, 16],
+ *   v_scales [B, Hkv, C32/32, d];  v_stage FP16 [B, Hkv, 32, d] (caller-owned, keeps the FP16
+ *   keys of the V-hat block that is still open between calls; contents undefined at L0 = 0).
+ * k_new, v_new: FP16 [B, Hkv, n, d] (k_new before RoPE when the tables are given: key t at
+ * position t).  K-hat rows are quantized as hifa4_quantize_qkv (or _rope) does; the V-hat blocks
+ * the new keys touch are quantized again from FP16, zero-padded past L0 + n.  After any sequence
+ * of appends the first L keys of the cache equal hifa4_quantize_qkv(_rope) of those L keys, byte
+ * for byte (K-hat scale bytes past L are unspecified; attention masks them).  Read it with
+ * hifa4_attention_fwd(_q16) and opts.kv_capacity = C.
+ * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE (L0 + n > C, short RoPE tables), HIFA4_ERR_UNSUPPORTED
+ * (d), HIFA4_ERR_ALIGNMENT, HIFA4_ERR_HIP.
+ */
+hifa4_status hifa4_cache_append(const hifa4_dims* dims, int64_t kv_capacity, const void* k_new, const void* v_new,
+                                const float* inv_s, const float* rope_cos, const float* rope_sin,
+                                int64_t rope_positions, void* k_codes, void* k_scales, void* v_codes,
+                                void* v_scales, void* v_stage, void* hip_stream);
 
 /* Number of KV splits hifa4_attention_fwd uses for these dims and options (1 when Lq > 1). */
 int32_t hifa4_decode_num_splits(const hifa4_dims* dims, const hifa4_attn_opts* opts);

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -140,6 +140,30 @@ def test_quantize_rope_rejects_bad_arguments(L):
     st = L.hifa4_quantize_qkv_rope(ctypes.byref(dims), None, None, ok, None, None, None, None, 0, None, None, None,
                                    None, None, None, None)
     assert st == 1  # v outputs missing, checked before any launch
+
+
+def test_cache_append_rejects_bad_arguments(L):
+    ok = ctypes.c_void_p(256)
+    ptrs = [ok] * 2 + [None, None, None] + [ok] * 5  # k_new, v_new, inv_s, cos, sin | 5 cache buffers
+    dims = hf.make_dims(2, 8, 2, 128, 1, 100)  # len_q = keys appended, len_kv = keys present
+
+    def app(dm, cap, p, n_pos=0):
+        return L.hifa4_cache_append(ctypes.byref(dm), cap, *p[:5], n_pos, *p[5:], None)
+    assert app(dims, 100, ptrs) == 2  # 100 + 1 > capacity
+    assert app(hf.make_dims(2, 8, 2, 96, 1, 10), 128, ptrs) == 3  # head_dim
+    bad = list(ptrs)
+    bad[9] = None  # stage missing
+    assert app(dims, 128, bad) == 1
+    rope = list(ptrs)
+    rope[3] = ok
+    assert app(dims, 128, rope) == 1  # one table without the other
+    rope[4] = ok
+    assert app(dims, 128, rope, n_pos=100) == 2  # tables must cover position 100
+    mis = list(ptrs)
+    mis[7] = ctypes.c_void_p(264)
+    assert app(dims, 128, mis) == 6
+    o = hf.make_opts(causal=True, kv_capacity=99)
+    assert L.hifa4_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(o)) == 0  # capacity < len_kv
 
 
 @pytest.mark.parametrize("cfg_id", [0, 1, 3])
