@@ -207,6 +207,45 @@ def bench_rope(args):
     return res
 
 
+def bench_append(args):
+    """hifa4_cache_append of one key per sequence (the decode loop's cache update): B64 Hkv8 d128,
+    RoPE and Smooth-QK on the key, the open V-hat block re-quantized from its FP16 stage.  The
+    cost does not depend on the cache length, so a 1024-key cache is cycled through."""
+    import torch
+    import bit_quantized_flashattention_amd as hf
+    import synth
+
+    cfg = synth.config(4)
+    b, hkv, d = cfg["B"], cfg["Hkv"], cfg["d"]
+    cap = 1024
+    cache = hf.make_cache(b, hkv, d, cap)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    kn = torch.randn((b, hkv, 1, d), generator=gen, device="cuda").to(torch.float16)
+    vn = torch.randn((b, hkv, 1, d), generator=gen, device="cuda").to(torch.float16)
+    invd = torch.ones((hkv, d), dtype=torch.float32, device="cuda")
+    cos32, sin32 = synth.rope_table(cfg["rope_theta"], cap, d)
+    cosd, sind = torch.from_numpy(cos32).cuda(), torch.from_numpy(sin32).cuda()
+
+    def step():
+        if cache["length"] == cap:
+            cache["length"] = 0
+        hf.cache_append(cache, kn, vn, invd, cosd, sind)
+
+    for _ in range(64):
+        step()
+    torch.cuda.synchronize()
+    n = 256  # eight full 32-key cycles of the open V-hat block
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"workload": "append 1 key per sequence, B%d Hkv%d d%d, RoPE + Smooth-QK on K, V-hat block re-quantized"
+                        % (b, hkv, d), "us_per_call": round(e0.elapsed_time(e1) / n * 1e3, 2)}
+
+
 def bench_decode(args):
     import torch
     import bit_quantized_flashattention_amd as hf
@@ -349,6 +388,7 @@ def main():
         line["rope_prefill"] = bench_rope(args)
     if not args.no_decode:
         line["decode"] = bench_decode(args)
+        line["decode"]["cache_append"] = bench_append(args)
     if args.traffic_probe:
         copy_probe()
     print(json.dumps(line), flush=True)
