@@ -3,13 +3,15 @@
 [HiFA4] Abstract, Theorem 1: with l taken from the higher-precision probabilities (the
 inconsistent formulation) and O from P-hat V, every channel of a row is scaled by the same
 factor; the abstract measures the per-tile error epsilon = sum(P-hat)/sum(P) - 1 as a net
-probability-mass loss.  This test runs the full workload twice through the C ABI, P-Reordered
-and inconsistent, with per-(16-row block, tile) statistics, and reports:
+probability-mass loss, and contrasts HiFA4 with direct 4-bit quantization.  This test runs the
+full workload through the C ABI, P-Reordered and inconsistent with per-(16-row block, tile)
+statistics, plus the same two without Smooth-QK (no smoothing + inconsistent is the direct
+formulation), and reports:
 
 * epsilon over all visited tiles (median, mean, p5, p95, fraction below 0); m does not depend on
   l, so both runs must produce identical tile sums;
-* the error of both outputs against unquantized FP32 softmax attention (oracle.reference_fp32 on
-  the original FP16 inputs) on sampled heads.
+* the error of the four outputs against unquantized FP32 softmax attention
+  (oracle.reference_fp32 on the original FP16 inputs) on sampled heads.
 
 The magnitude of epsilon has no value on the pages for synthetic inputs (parity unpinned); the
 test checks the sign the abstract reports and that the tile sums of the two runs agree.  Set
@@ -65,7 +67,15 @@ def test_accuracy_report_batched_prefill():
     assert eps_report["median"] < 0, "P-hat flushes small probabilities: a net mass loss per tile"
 
     # error against unquantized FP32 attention on sampled heads (all rows of each)
-    err = {"p_reordered": [], "inconsistent": []}
+    # the direct formulation the abstract contrasts HiFA4 with: no Smooth-QK, l from the
+    # unquantized probabilities
+    res_direct = hf.quantize_qkv(q, k, v, None, None, dims=dims)
+    out_direct = hf.attention_fwd(res_direct, dims, True, A.INCONSISTENT, cfg["kv_tile"])
+    res_nosmooth_pr = hf.attention_fwd(res_direct, dims, True, A.P_REORDERED, cfg["kv_tile"])
+    torch.cuda.synchronize()
+    runs["direct"] = (out_direct, None)
+    runs["no_smooth_p_reordered"] = (res_nosmooth_pr, None)
+    err = {"p_reordered": [], "inconsistent": [], "no_smooth_p_reordered": [], "direct": []}
     heads = [(0, 0), (2, 9), (5, 22), (7, 31)]
     group = hq // hkv
     for (b, h) in heads:
