@@ -8,7 +8,7 @@
  * state (running max m, normalizer l, rescaled output O) in FP16.  The normalizer is accumulated
  * from the same quantized probabilities P-hat that enter the PV product (P-Reordering).
  *
- * 4-bit format (the pages name it HIF4 without a bit layout; this library substitutes): E2M1
+ * 4-bit format (the HiFA4 abstract names it HIF4 without a bit layout; this library substitutes): E2M1
  * codes (sign, 2 exponent bits, 1 mantissa bit: 0, .5, 1, 1.5, 2, 3, 4, 6) with one
  * power-of-two E8M0 scale byte (2^(byte-127)) per block of 32 elements; two codes per byte,
  * the lower-index element in the low nibble.
@@ -134,8 +134,8 @@ hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, cons
                                      void* v_scales, void* hip_stream);
 
 /*
- * Append keys to a 4-bit K-hat / V-hat cache (device, async).  The step after prefill in decoding
- * (the pages' decode workload reads a pre-quantized cache).  dims->len_kv = keys already in the
+ * Append keys to a 4-bit K-hat / V-hat cache (device, async): in decoding, each new token's key
+ * and value join the quantized cache before its attention.  dims->len_kv = keys already in the
  * cache (L0), dims->len_q = keys appended (n >= 1); heads_q is not used.  The cache buffers use
  * the layouts above with Lk replaced by kv_capacity (C >= L0 + n) for the strides:
  *   k_codes [B, Hkv, C, d/2], k_scales [B, Hkv, d/32, C32], v_codes [B, Hkv, C32/32, d, 16],
