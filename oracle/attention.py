@@ -155,11 +155,11 @@ class Quantized:
                 kscale, np.ascontiguousarray(vcode), np.ascontiguousarray(vscale))
 
 
-def quantize_qkv(q, k, v, s32=None, inv32=None):
+def quantize_qkv(q, k, v, s32=None, inv32=None, rule="no_clip"):
     """Smooth-QK (if scales given) then 4-bit block quantization.
 
     q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d] hold FP16 values.  Q and K are
-    blocked along d, V along tokens.
+    blocked along d, V along tokens.  ``rule``: the block scale rule (mx.SCALE_RULES).
     """
     from . import smooth
     q = np.asarray(q)
@@ -174,12 +174,12 @@ def quantize_qkv(q, k, v, s32=None, inv32=None):
     else:
         qs = q.astype(F32)
         ks = k.astype(F32)
-    qc, qe = mx.quantize_blocks(qs.astype(F64))
-    kc, ke = mx.quantize_blocks(ks.astype(F64))
+    qc, qe = mx.quantize_blocks(qs.astype(F64), rule)
+    kc, ke = mx.quantize_blocks(ks.astype(F64), rule)
     lk32 = -(-lk // 32) * 32
     vt = np.zeros((b, hkv, d, lk32), dtype=F64)
     vt[..., :lk] = np.swapaxes(v.astype(F64), 2, 3)
-    vc, ve = mx.quantize_blocks(vt)
+    vc, ve = mx.quantize_blocks(vt, rule)
     return Quantized(qc, qe, kc, ke, vc, ve, lk)
 
 

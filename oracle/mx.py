@@ -13,6 +13,11 @@ Readings where the pages are silent:
 * element rounding: round to nearest, ties to the even code, saturating at 6;
 * the sign bit is copied from the input (so -0.0 and tiny negatives give 0x8);
 * packing: byte = code[2i] | code[2i+1] << 4; scale byte = e + 127.
+
+Accuracy variant (rule "floor"): the shared-exponent rule of the OCP microscaling format,
+e = floor(log2 amax) - 2 (2 = the largest E2M1 exponent), clamped the same way; magnitudes in
+(6, 8) * 2**e then saturate to 6.  It is not the method's rule: it clips up to a quarter of the
+block maximum, and it serves the comparison of the two rules.
 """
 
 import numpy as np
@@ -35,6 +40,19 @@ def scale_exponent(amax):
     e_nz = np.where(M <= 1.5, E - 2, E - 1)
     e[nz] = np.clip(e_nz, -127, 127)
     return e
+
+
+def scale_exponent_floor(amax):
+    """OCP microscaling shared exponent: floor(log2 amax) - 2, clamped; -127 for a zero block."""
+    amax = np.asarray(amax, dtype=F64)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    _, E = np.frexp(amax[nz])  # amax = m * 2**E, m in [0.5, 1): floor(log2 amax) = E - 1
+    e[nz] = np.clip(E.astype(np.int64) - 1 - 2, -127, 127)
+    return e
+
+
+SCALE_RULES = {"no_clip": scale_exponent, "floor": scale_exponent_floor}
 
 
 def rne_code(y):
@@ -65,8 +83,8 @@ def code_half_units(code):
     return np.where(code & 8, -v, v)
 
 
-def quantize_blocks(x):
-    """Quantize along the last axis (length a multiple of 32).
+def quantize_blocks(x, rule="no_clip"):
+    """Quantize along the last axis (length a multiple of 32) with a scale rule of SCALE_RULES.
 
     Returns (codes uint8 [..., n], exponents int64 [..., n // 32]).
     """
@@ -75,7 +93,7 @@ def quantize_blocks(x):
     assert n % BLOCK == 0, "block axis must be a multiple of 32"
     xb = x.reshape(x.shape[:-1] + (n // BLOCK, BLOCK))
     amax = np.abs(xb).max(axis=-1)
-    e = scale_exponent(amax)
+    e = SCALE_RULES[rule](amax)
     y = xb * np.exp2(-e.astype(F64))[..., None]  # exact power-of-two scaling
     codes = rne_code(y).reshape(x.shape)
     return codes, e

@@ -95,3 +95,44 @@ def test_pack_roundtrip_and_zero_block():
     assert np.array_equal(mx.unpack_codes(mx.pack_codes(codes)), codes)
     c, e = mx.quantize_blocks(np.zeros((1, 32)))
     assert e[0, 0] == -127 and mx.scale_bytes(e)[0, 0] == 0 and not c.any()
+
+
+def brute_scale_floor(amax):
+    """Search: the e with 4 * 2**e <= amax < 8 * 2**e (E2M1's top binade holds the maximum), clamped."""
+    out = []
+    for a in np.asarray(amax, dtype=np.float64):
+        if a == 0:
+            out.append(-127)
+            continue
+        e = -200
+        while not (a < 8.0 * 2.0 ** e):
+            e += 1
+        assert 4.0 * 2.0 ** e <= a or e == -200
+        out.append(min(max(e, -127), 127))
+    return np.array(out)
+
+
+def test_floor_rule_matches_search_and_ocp_examples():
+    rng = np.random.default_rng(31)
+    amax = np.concatenate([np.exp2(rng.uniform(-120, 120, 2000)),
+                           np.array([6.0, 7.0, 7.9999, 8.0, 4.0, 3.9999, 1.0, 0.0])])
+    assert np.array_equal(mx.scale_exponent_floor(amax), brute_scale_floor(amax))
+    # OCP examples: 6 -> e = 0 (6 kept); 7 -> e = 0 and 7 saturates to 6; 8 -> e = 1 (4 kept)
+    codes, e = mx.quantize_blocks(np.array([[6.0] + [0.0] * 31, [7.0] + [0.0] * 31, [8.0] + [0.0] * 31]), "floor")
+    assert list(e[:, 0]) == [0, 0, 1]
+    assert list(codes[:, 0]) == [7, 7, 6]  # 6, 6 (saturated), 4
+
+
+def test_floor_rule_clips_where_the_method_rule_does_not():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((400, 32)) * np.exp2(rng.integers(-10, 10, (400, 1)))
+    c_f, e_f = mx.quantize_blocks(x, "floor")
+    c_n, e_n = mx.quantize_blocks(x, "no_clip")
+    amax = np.abs(x).max(axis=1)
+    # floor never exceeds the method's exponent, and is one below it exactly when amax / 2^floor > 6
+    assert np.all(e_f[:, 0] <= e_n[:, 0]) and np.all(e_n[:, 0] - e_f[:, 0] <= 1)
+    clip = amax > 6.0 * np.exp2(e_f[:, 0])
+    assert np.array_equal(clip, e_n[:, 0] == e_f[:, 0] + 1)
+    # clipped blocks saturate their maximum at 6 * 2^e
+    deq = mx.dequantize_blocks(c_f, e_f)
+    assert np.all(np.abs(deq).max(axis=1) <= 6.0 * np.exp2(e_f[:, 0]))
