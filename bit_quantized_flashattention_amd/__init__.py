@@ -49,6 +49,8 @@ def lib():
         L.hifa4_calibrate.restype = ctypes.c_int
         L.hifa4_quantize_qkv.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 11
         L.hifa4_quantize_qkv.restype = ctypes.c_int
+        L.hifa4_quantize_qkv_rule.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32] + [_vp] * 12
+        L.hifa4_quantize_qkv_rule.restype = ctypes.c_int
         L.hifa4_quantize_qkv_rope.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 7 + [ctypes.c_int64] + [_vp] * 7
         L.hifa4_quantize_qkv_rope.restype = ctypes.c_int
         L.hifa4_cache_append.argtypes = [ctypes.POINTER(Dims), ctypes.c_int64] + [_vp] * 5 + [ctypes.c_int64] + [_vp] * 6
@@ -130,7 +132,10 @@ def quantized_shapes(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
     }
 
 
-def quantize_qkv(q=None, k=None, v=None, s=None, inv_s=None, dims=None, out=None, stream=None):
+SCALE_NO_CLIP, SCALE_FLOOR = 0, 1
+
+
+def quantize_qkv(q=None, k=None, v=None, s=None, inv_s=None, dims=None, out=None, stream=None, scale_rule=SCALE_NO_CLIP):
     """Smooth-QK rescale + 4-bit quantization on the GPU.
 
     q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d]: contiguous CUDA float16 tensors (any may be None
@@ -154,8 +159,8 @@ def quantize_qkv(q=None, k=None, v=None, s=None, inv_s=None, dims=None, out=None
             res[name] = torch.empty(shp, dtype=torch.uint8, device=dev)
     if (s is None) != (inv_s is None):
         raise ValueError("pass both s and inv_s or neither")
-    _check(lib().hifa4_quantize_qkv(
-        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(inv_s),
+    _check(lib().hifa4_quantize_qkv_rule(
+        ctypes.byref(dims), int(scale_rule), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(inv_s),
         _ptr(res.get("q_codes") if q is not None else None), _ptr(res.get("q_scales") if q is not None else None),
         _ptr(res.get("k_codes") if k is not None else None), _ptr(res.get("k_scales") if k is not None else None),
         _ptr(res.get("v_codes") if v is not None else None), _ptr(res.get("v_scales") if v is not None else None),

@@ -26,6 +26,17 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// The shared-exponent rule of the OCP microscaling format, an accuracy variant: e = floor(log2
+// amax) - 2 (2 = the largest E2M1 exponent), clamped; -127 for an all-zero block.  Magnitudes in
+// (6, 8) * 2^e then saturate to 6 in the conversion.
+__device__ __forceinline__ int mx_exponent_floor(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int ex;
+  (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+  const int e = ex - 3;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // 2^e as the FP32 scale operand of the FP4 converter, which reads the operand's biased exponent
 // field as an E8M0 value (e = -127 is the subnormal 2^-127, exponent field 0).
 __device__ __forceinline__ float e8m0_as_float(int e) {
@@ -73,11 +84,11 @@ __device__ __forceinline__ void load_block32(const uint16_t* x, const float* s, 
 // 4-bit quantization of 32 FP32 values: the block exponent comes from the largest magnitude and
 // the codes are RNE onto E2M1 relative to 2^e.  Returns the E8M0 scale byte (e + 127); the 16
 // code bytes go to *codes (element 2i in the low nibble of byte i).
-__device__ __forceinline__ uint32_t quantize_values32(const float* v, uint4* codes) {
+__device__ __forceinline__ uint32_t quantize_values32(const float* v, uint4* codes, bool floor_rule = false) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-  const int e = mx_exponent(amax);
+  const int e = floor_rule ? mx_exponent_floor(amax) : mx_exponent(amax);
   const float scale = e8m0_as_float(e);
   codes->x = pack8_fp4(v + 0, scale);
   codes->y = pack8_fp4(v + 8, scale);
@@ -101,7 +112,8 @@ __device__ __forceinline__ void unpack_block32(const Block32In& in, float* v) {
 
 // Smooth-QK rescale and 4-bit quantization of one loaded block (scaled: apply in.s).  Each value
 // becomes fp32(x * s) (one rounding; contraction is off), then quantize_values32.
-__device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool scaled, uint4* codes) {
+__device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool scaled, uint4* codes,
+                                                      bool floor_rule = false) {
   float v[32];
   unpack_block32(in, v);
   if (scaled) {
@@ -113,7 +125,7 @@ __device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool 
       v[4 * i + 3] = v[4 * i + 3] * in.s[i].w;
     }
   }
-  return quantize_values32(v, codes);
+  return quantize_values32(v, codes, floor_rule);
 }
 
 // RoPE (rotate-half, FP32), Smooth-QK and 4-bit quantization of block blk of one FP16 row of

@@ -176,12 +176,14 @@ hifa4_status hifa4_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64
   return ok();
 }
 
-hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const void* k, const void* v,
-                                const float* s, const float* inv_s, void* q_codes, void* q_scales,
-                                void* k_codes, void* k_scales, void* v_codes, void* v_scales,
-                                void* hip_stream) {
+hifa4_status hifa4_quantize_qkv_rule(const hifa4_dims* dims, int32_t scale_rule, const void* q, const void* k,
+                                     const void* v, const float* s, const float* inv_s, void* q_codes,
+                                     void* q_scales, void* k_codes, void* k_scales, void* v_codes,
+                                     void* v_scales, void* hip_stream) {
   hifa4_status st = check_dims(dims);
   if (st != HIFA4_OK) return st;
+  if (scale_rule != HIFA4_SCALE_NO_CLIP && scale_rule != HIFA4_SCALE_FLOOR)
+    return fail(HIFA4_ERR_SHAPE, "quantize: scale_rule must be HIFA4_SCALE_NO_CLIP or HIFA4_SCALE_FLOOR");
   if ((s == nullptr) != (inv_s == nullptr)) return fail(HIFA4_ERR_NULL, "quantize: pass both s and inv_s or neither");
   if (q && (!q_codes || !q_scales)) return fail(HIFA4_ERR_NULL, "quantize: q outputs are NULL");
   if (k && (!k_codes || !k_scales)) return fail(HIFA4_ERR_NULL, "quantize: k outputs are NULL");
@@ -193,24 +195,33 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
   if (q) {
     hifa4::QuantRowsArgs a{(const uint16_t*)q, s, (int64_t)dims->batch * dims->heads_q * dims->len_q,
                            dims->len_q, round32(dims->len_q), dims->heads_q, group, dims->head_dim, 0,
-                           (uint8_t*)q_codes, (uint8_t*)q_scales};
+                           (uint8_t*)q_codes, (uint8_t*)q_scales, scale_rule};
     hipError_t e = hifa4::launch_quantize_rows(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
   }
   if (k) {
     hifa4::QuantRowsArgs a{(const uint16_t*)k, inv_s, (int64_t)dims->batch * dims->heads_kv * dims->len_kv,
                            dims->len_kv, round32(dims->len_kv), dims->heads_kv, 1, dims->head_dim, 1,
-                           (uint8_t*)k_codes, (uint8_t*)k_scales};
+                           (uint8_t*)k_codes, (uint8_t*)k_scales, scale_rule};
     hipError_t e = hifa4::launch_quantize_rows(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
   }
   if (v) {
     hifa4::QuantVtArgs a{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
-                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales};
+                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales,
+                         scale_rule};
     hipError_t e = hifa4::launch_quantize_vt(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize v: ") + hipGetErrorString(e));
   }
   return ok();
+}
+
+hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const void* k, const void* v,
+                                const float* s, const float* inv_s, void* q_codes, void* q_scales,
+                                void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                                void* hip_stream) {
+  return hifa4_quantize_qkv_rule(dims, HIFA4_SCALE_NO_CLIP, q, k, v, s, inv_s, q_codes, q_scales, k_codes,
+                                 k_scales, v_codes, v_scales, hip_stream);
 }
 
 hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, const void* k, const void* v,

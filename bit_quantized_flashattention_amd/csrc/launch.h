@@ -18,6 +18,7 @@ struct QuantRowsArgs {
   int32_t block_planes; // 0: scales [rows, d/32] (Q-hat); 1: [B*H, d/32, len32] (K-hat), tail 0
   uint8_t* codes;       // [rows, d/2]
   uint8_t* scales;
+  int32_t scale_rule;   // 0: no-clip (the method); 1: OCP floor rule (accuracy variant)
 };
 
 struct QuantVtArgs {
@@ -28,6 +29,7 @@ struct QuantVtArgs {
   int32_t d;
   uint8_t* codes;       // [B*Hkv, len32/32, d, 16] (block-major)
   uint8_t* scales;      // [B*Hkv, len32/32, d]
+  int32_t scale_rule;   // as in QuantRowsArgs
 };
 
 struct AttnArgs {

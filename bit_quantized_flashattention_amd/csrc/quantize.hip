@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
     load_block32(nullptr, a.scale + (int64_t)(h / a.heads_per_scale_row) * D + blk * kBlock, in);
   }
   uint4 out;
-  const uint32_t e8 = quantize_loaded32(in, a.scale != nullptr, &out);
+  const uint32_t e8 = quantize_loaded32(in, a.scale != nullptr, &out, a.scale_rule == 1);
   *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + blk * 16) = out;
   *scale_dst = (uint8_t)e8;
 }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
       v[i] = (float)tile[(jb * kBlock + i) * ROW + ch];
       amax = fmaxf(amax, fabsf(v[i]));
     }
-    const int e = mx_exponent(amax);
+    const int e = a.scale_rule == 1 ? mx_exponent_floor(amax) : mx_exponent(amax);
     const float sc = e8m0_as_float(e);
     uint4 out;
     out.x = pack8_fp4(v + 0, sc);

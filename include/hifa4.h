@@ -114,6 +114,22 @@ hifa4_status hifa4_quantize_qkv(const hifa4_dims* dims, const void* q, const voi
                                 void* q_codes, void* q_scales, void* k_codes, void* k_scales,
                                 void* v_codes, void* v_scales, void* hip_stream);
 
+/* Block scale rules of hifa4_quantize_qkv_rule. */
+enum { HIFA4_SCALE_NO_CLIP = 0, HIFA4_SCALE_FLOOR = 1 };
+
+/*
+ * hifa4_quantize_qkv with a choice of block scale rule, for accuracy comparisons.
+ * HIFA4_SCALE_NO_CLIP is the rule above (the method's: no element is clipped);
+ * HIFA4_SCALE_FLOOR is the shared-exponent rule of the OCP microscaling format,
+ * e = floor(log2 max|x|) - 2 clamped to [-127, 127] (-127 for a zero block), whose codes saturate
+ * at 6 for magnitudes in (6, 8) * 2^e.  Errors: those of hifa4_quantize_qkv; HIFA4_ERR_SHAPE for
+ * another rule.
+ */
+hifa4_status hifa4_quantize_qkv_rule(const hifa4_dims* dims, int32_t scale_rule, const void* q, const void* k,
+                                     const void* v, const float* s, const float* inv_s, void* q_codes,
+                                     void* q_scales, void* k_codes, void* k_scales, void* v_codes,
+                                     void* v_scales, void* hip_stream);
+
 /*
  * RoPE, Smooth-QK rescale and 4-bit quantization from pre-RoPE inputs, fused (device, async).
  * [HiFA4 Abstract: Smooth-QK rescales Q and K per channel after RoPE, and at inference only an

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -119,6 +119,9 @@ def test_quantize_rejects_bad_arguments(L):
     bad = hf.make_dims(1, 4, 2, 80, 64, 64)
     st = L.hifa4_quantize_qkv(ctypes.byref(bad), dummy, None, None, None, None, dummy, dummy, None, None, None, None, None)
     assert st == 3
+    st = L.hifa4_quantize_qkv_rule(ctypes.byref(dims), 2, dummy, None, None, None, None, dummy, dummy, None, None, None,
+                                   None, None)
+    assert st == 2 and b"scale_rule" in L.hifa4_last_error()
 
 
 def test_quantize_rope_rejects_bad_arguments(L):

@@ -170,3 +170,28 @@ def test_quantizer_edge_values():
     inv = (1.0 / s.astype(np.float64)).astype(np.float32)
     res = gpu_quantize(q, k, v, s, inv)
     assert_codes_equal(res, A.quantize_qkv(q, k, v, s, inv))
+
+
+def test_floor_scale_rule_saturation_and_attention():
+    """The OCP floor scale rule (accuracy variant): block maxima in (6, 8) * 2^e saturate at code 6;
+    codes bit-exact against the oracle's floor rule, attention from them within tolerance."""
+    import torch
+    from gpu_helpers import to_dev
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((1, 4, 96, 64)).astype(np.float16)
+    k = rng.standard_normal((1, 2, 130, 64)).astype(np.float16)
+    v = rng.standard_normal((1, 2, 130, 64)).astype(np.float16)
+    for i, m in enumerate([7.0, 7.99, 6.5, 8.0, 6.0, 4.0, 5.99]):
+        q[0, 0, i, 0] = m
+        q[0, 1, i, 33] = -m
+        k[0, 0, i, 7] = m
+        v[0, 1, 32 + i, 9] = -m
+    q[0, 2, 0] = 0
+    print("case floor scale rule", flush=True)
+    dims = hf.make_dims(1, 4, 2, 64, 96, 130)
+    res = hf.quantize_qkv(to_dev(q), to_dev(k), to_dev(v), dims=dims, scale_rule=hf.SCALE_FLOOR)
+    qq = A.quantize_qkv(q, k, v, rule="floor")
+    assert_codes_equal(res, qq)
+    out = hf.attention_fwd(res, dims, True, 0, 64)
+    torch.cuda.synchronize()
+    compare_out(out.cpu().numpy(), A.attention_p(qq, True, 64, 0), "floor-rule")
