@@ -53,6 +53,8 @@ float half_bits_to_float(uint16_t h) {
   return f;
 }
 
+int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
+
 hifa4_status check_dims(const hifa4_dims* d) {
   if (d == nullptr) return fail(HIFA4_ERR_NULL, "dims is NULL");
   if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->len_q < 1 || d->len_kv < 1)
@@ -63,12 +65,16 @@ hifa4_status check_dims(const hifa4_dims* d) {
     return fail(HIFA4_ERR_UNSUPPORTED, "heads_q / heads_kv must be <= 8 or a multiple of 8");
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
     return fail(HIFA4_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
-  if (d->len_q > (int64_t)1 << 31 || d->len_kv > (int64_t)1 << 31)
-    return fail(HIFA4_ERR_SHAPE, "lengths must be <= 2^31");
+  if (d->len_q >= (int64_t)1 << 31 || d->len_kv >= (int64_t)1 << 31)
+    return fail(HIFA4_ERR_SHAPE, "lengths must be < 2^31");
+  // the kernels address one (batch, KV head) slice of K-hat / V-hat codes with 32-bit offsets
+  if (round32(d->len_kv) * (d->head_dim / 2) >= (int64_t)1 << 31)
+    return fail(HIFA4_ERR_SHAPE, "len_kv * head_dim / 2 must stay below 2^31 bytes per (batch, KV head)");
+  if (d->batch > 65535 || d->heads_q > 65535)
+    return fail(HIFA4_ERR_SHAPE, "batch and heads_q must be <= 65535 (launch grid limits)");
   return HIFA4_OK;
 }
 
-int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
 
 int32_t auto_splits(const hifa4_dims* d, int kv_tile) {
   // enough (batch, KV head, split) work-groups to cover the 256 compute units several times,
@@ -89,8 +95,9 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
   if (o->kv_tile != 64 && o->kv_tile != 128) return fail(HIFA4_ERR_UNSUPPORTED, "kv_tile must be 64 or 128");
   if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
-  if (o->kv_capacity != 0 && (o->kv_capacity < d->len_kv || o->kv_capacity > (int64_t(1) << 31)))
-    return fail(HIFA4_ERR_SHAPE, "kv_capacity must be 0 or in [len_kv, 2^31]");
+  if (o->kv_capacity != 0 &&
+      (o->kv_capacity < d->len_kv || round32(o->kv_capacity) * (d->head_dim / 2) >= (int64_t(1) << 31)))
+    return fail(HIFA4_ERR_SHAPE, "kv_capacity must be 0 or at least len_kv, with kv_capacity * head_dim / 2 below 2^31");
   return HIFA4_OK;
 }
 
@@ -276,8 +283,8 @@ hifa4_status hifa4_cache_append(const hifa4_dims* dims, int64_t kv_capacity, con
     return fail(HIFA4_ERR_SHAPE, "append: need batch, heads_kv, len_q (new keys) >= 1 and len_kv >= 0");
   if (dims->head_dim != 64 && dims->head_dim != 128 && dims->head_dim != 256)
     return fail(HIFA4_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
-  if (dims->len_kv + dims->len_q > kv_capacity || kv_capacity > (int64_t(1) << 31))
-    return fail(HIFA4_ERR_SHAPE, "append: len_kv + len_q must not exceed kv_capacity (<= 2^31)");
+  if (dims->len_kv + dims->len_q > kv_capacity || round32(kv_capacity) * (dims->head_dim / 2) >= (int64_t(1) << 31))
+    return fail(HIFA4_ERR_SHAPE, "append: len_kv + len_q must not exceed kv_capacity (kv_capacity * head_dim / 2 < 2^31)");
   if (!k_new || !v_new || !k_codes || !k_scales || !v_codes || !v_scales || !v_stage)
     return fail(HIFA4_ERR_NULL, "append: a tensor pointer is NULL");
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(HIFA4_ERR_NULL, "append: pass both RoPE tables or neither");

@@ -100,6 +100,19 @@ def test_attention_rejects_bad_arguments_without_launching(L):
     assert L.hifa4_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(opts)) == 0
 
 
+def test_size_limits_are_rejected(L):
+    dummy = ctypes.c_void_p(256)
+    o = hf.make_opts(causal=False)
+    for dm in [hf.make_dims(1, 4, 2, 256, 16, 1 << 24),  # a K-hat slice of 2^31 bytes
+               hf.make_dims(1, 4, 2, 128, 1 << 31, 64),
+               hf.make_dims(70000, 4, 2, 128, 16, 64),
+               hf.make_dims(1, 70000 * 8, 8, 128, 16, 64)]:
+        st = L.hifa4_attention_fwd(ctypes.byref(dm), ctypes.byref(o), *([dummy] * 7), None, 0, None, None)
+        assert st in (2, 3), (dm.batch, dm.heads_q, dm.len_q, dm.len_kv, st)
+    ok = hf.make_dims(1, 4, 2, 256, 16, (1 << 24) - 32)
+    assert L.hifa4_attention_workspace_bytes(ctypes.byref(ok), ctypes.byref(o)) == 0  # valid prefill
+
+
 def test_decode_splits_resolution(L):
     d = hf.make_dims(64, 32, 8, 128, 1, 32768)
     assert hf.decode_num_splits(d, hf.make_opts(causal=True, num_splits=0)) >= 1
