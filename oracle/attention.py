@@ -46,7 +46,11 @@ Readings where the pages are silent (each is listed in the design notes):
 * causal masking is bottom-right aligned: key c is visible to query r iff
   c <= r + (Lk - Lq);
 * split-KV decode: splits cover whole tiles, each split runs the recurrence
-  from the empty state, and the FP16 partial states are merged in split order.
+  from the empty state, and the FP16 partial states are merged in split order;
+* accuracy variant (not the method's reading, used to measure what the integer
+  running max costs): m = the FP16 value nearest to fp32(max S * C), the
+  rescale alpha = rn16(2**rn16(fp32(m_old - m_new))), m + e rounded once to
+  FP32; prefill only (the split merge assumes integer maxima).
 
 Level "P" (parity) is what the GPU is compared against.  Level "S" (semantic)
 rounds only where a narrow format is stored (4-bit codes, FP16 state) and uses
@@ -63,6 +67,11 @@ F32 = np.float32
 F64 = np.float64
 P_REORDERED = 0
 INCONSISTENT = 1
+# running-max rules: the method's reading (the integer ceil(fp32(max S * C)), so that every
+# rescale is an exact power of two), and an accuracy variant that keeps the FP16 value nearest
+# to fp32(max S * C) instead (round-to-nearest running max)
+MAX_CEIL = 0
+MAX_NEAREST16 = 1
 STATS_ROWS = 16  # query rows per epsilon-statistics tile (a tile is 16 rows x kv_tile keys)
 
 
@@ -249,12 +258,16 @@ class Diag:
         self.stats = []  # (row_block, tile, sum_phat, sum_p)
 
 
-def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row_ids=None):
+def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row_ids=None, max_rule=MAX_CEIL):
     """Level-P tile loop for one head over tiles [tile_lo, tile_hi).
 
     s fp32 [R, Npad] scores, vis [R, Npad], vh int64 [d, Npad] V-hat codes in
     half units, ve int64 [d, Npad/32] V-hat block exponents.  Returns the FP16
-    state (m as FP32 integer values, l, O as FP16).
+    state (m as FP32 values -- integers under MAX_CEIL --, l, O as FP16).
+
+    max_rule MAX_NEAREST16 (accuracy variant): m_new = max(m, rn16(fp32(max S * C))), the rescale
+    is alpha = rn16(2**rn16(fp32(m - m_new))) (the FP16 exp2 of the FP32 difference), and
+    m_new + e is rounded once to FP32; everything else is as under MAX_CEIL.
     """
     r_n = s.shape[0]
     d = vh.shape[0]
@@ -269,17 +282,22 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
         anyv = vt.any(axis=1)
         smax = np.where(vt, st, F32(-np.inf)).max(axis=1).astype(F32)
         with np.errstate(invalid="ignore"):
-            tm = np.ceil(fp.mul32(smax, c32)).astype(F32)
+            prod = fp.mul32(smax, c32)
+            tm = (np.ceil(prod) if max_rule == MAX_CEIL else fp.rn16(prod)).astype(F32)
         m_new = np.where(anyv, np.maximum(m, tm), m).astype(F32)
-        with np.errstate(invalid="ignore", over="ignore"):
-            alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2((m - m_new).astype(F64))))
-        alpha = alpha.astype(F32)
-        alpha16 = fp.rn16(alpha)  # the state update runs in FP16
+        if max_rule == MAX_CEIL:
+            with np.errstate(invalid="ignore", over="ignore"):
+                alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2((m - m_new).astype(F64))))
+            alpha16 = fp.rn16(alpha.astype(F32))  # exact powers of two; the state update runs in FP16
+        else:
+            fin = np.isfinite(m) & np.isfinite(m_new)
+            diff = fp.add32(np.where(fin, m, F32(0)), -np.where(fin, m_new, F32(0)))
+            alpha16 = np.where(np.isneginf(m), np.float16(0), exp2_16(diff)).astype(np.float16)
         mm = np.where(np.isfinite(m_new), m_new, F32(0)).astype(F32)
         # P-hat: one power-of-two scale per (row, tile), from the tile's largest score
         top = np.where(anyv, smax, F32(0)).astype(F32)
         e_row = np.where(anyv, tile_exponent(fp.fma32(top, c32, -mm)), -127)
-        big_m = (mm.astype(F64) + e_row).astype(F32)  # integers: exact
+        big_m = fp.add32(mm, e_row.astype(F32))  # exact for integer m
         u = fp.fma32(np.where(vt, st, F32(0)), c32, -big_m[:, None])
         p16 = np.where(vt, exp2_16(u), np.float16(0))
         codes = np.where(vt, mx.rne_code(p16.astype(F64)), 0).astype(np.uint8)
@@ -320,10 +338,12 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
     return State(m, l16, o16)
 
 
-def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True, round_state=True):
+def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True, round_state=True,
+                 max_rule=MAX_CEIL):
     """Level-S tile loop: exact scores and exp2, rounding only where a narrow format is stored.
 
-    vvals FP64 [Npad, d] (dequantized V-hat, or the raw V for the identity quantizer).
+    vvals FP64 [Npad, d] (dequantized V-hat, or the raw V for the identity quantizer).  Under
+    MAX_NEAREST16 the running max is the FP16 rounding of max S * C (m is stored in FP16).
     """
     r_n = s64.shape[0]
     d = vvals.shape[1]
@@ -338,7 +358,8 @@ def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True
         anyv = vt.any(axis=1)
         smax = np.where(vt, st, -np.inf).max(axis=1)
         with np.errstate(invalid="ignore"):
-            m_new = np.where(anyv, np.maximum(m, np.ceil(smax * c64)), m)
+            top = np.ceil(smax * c64) if max_rule == MAX_CEIL else (smax * c64).astype(np.float16).astype(F64)
+            m_new = np.where(anyv, np.maximum(m, top), m)
             alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2(m - m_new)))
         mm = np.where(np.isfinite(m_new), m_new, 0.0)
         p = np.where(vt, np.exp2(np.where(vt, st, 0.0) * c64 - mm[:, None]), 0.0)
@@ -396,8 +417,11 @@ def split_tiles(n_tiles, num_splits):
     return [(min(s * per, n_tiles), min((s + 1) * per, n_tiles)) for s in range(num_splits)]
 
 
-def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, stats=False):
-    """Level-P output rows of one (batch, query head): FP16 [len(rows), d]."""
+def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, stats=False, max_rule=MAX_CEIL):
+    """Level-P output rows of one (batch, query head): FP16 [len(rows), d].
+
+    MAX_NEAREST16 is defined for the unsplit (prefill) loop only.
+    """
     hq = qq.qc.shape[1]
     hkv = qq.kc.shape[1]
     g = h // (hq // hkv)
@@ -421,19 +445,21 @@ def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, 
         diag.total_s += int(vis[:, :lk].sum())
     c32 = softmax_scale_log2(d)
     if num_splits <= 1:
-        st = recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, 0, n_tiles, diag, rows if stats else None)
+        st = recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, 0, n_tiles, diag, rows if stats else None, max_rule)
         return finish(st, "P")
+    assert max_rule == MAX_CEIL, "the split-KV merge is defined for integer running maxima"
     states = [recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, lo, hi, diag) for lo, hi in split_tiles(n_tiles, num_splits)]
     return finish(merge_splits(states), "P")
 
 
-def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None):
+def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None, max_rule=MAX_CEIL):
     """Full Level-P output FP16 [B, Hq, Lq, d]."""
     b_n, hq, lq, d = qq.qc.shape
     out = np.zeros((b_n, hq, lq, d), dtype=np.float16)
     for b in range(b_n):
         for h in range(hq):
-            out[b, h] = attention_head_p(qq, b, h, np.arange(lq), causal, bc, mode, num_splits, diag)
+            out[b, h] = attention_head_p(qq, b, h, np.arange(lq), causal, bc, mode, num_splits, diag,
+                                         max_rule=max_rule)
     return out
 
 
@@ -445,7 +471,8 @@ def tile_stats_p(qq, causal, bc, b, h):
     return diag.stats
 
 
-def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_state=True, num_splits=1):
+def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_state=True, num_splits=1,
+                max_rule=MAX_CEIL):
     """Level-S output for one head from values: qv [Lq, d], kv [Lk, d], vv [Lk, d] (FP64 values).
 
     With quantize=False and round_state=False this is textbook softmax attention.
@@ -461,10 +488,10 @@ def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_s
     vpad[:lk] = vv
     c64 = math.log2(math.e) / math.sqrt(d)
     if num_splits <= 1:
-        st = recurrence_s(s, vis, vpad, c64, bc, mode, 0, n_tiles, quantize, round_state)
+        st = recurrence_s(s, vis, vpad, c64, bc, mode, 0, n_tiles, quantize, round_state, max_rule)
         return st.o / st.l[:, None] if not round_state else finish(st, "S")
     # split + exact merge (Level S keeps the partials in FP64)
-    parts = [recurrence_s(s, vis, vpad, c64, bc, mode, lo, hi, quantize, round_state)
+    parts = [recurrence_s(s, vis, vpad, c64, bc, mode, lo, hi, quantize, round_state, max_rule)
              for lo, hi in split_tiles(n_tiles, num_splits) if hi > lo]
     m = np.max([p.m for p in parts], axis=0)
     o = sum(np.exp2(p.m - m)[:, None] * p.o for p in parts)
