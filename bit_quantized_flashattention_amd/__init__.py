@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libhifa4.so")
 
 P_REORDERED = 0
 INCONSISTENT = 1
+MAX_CEIL, MAX_NEAREST16 = 0, 1  # running-max rules (hifa4.h)
 
 
 class Dims(ctypes.Structure):
@@ -30,7 +31,7 @@ class Dims(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("normalizer", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64)]
+                ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64), ("max_rule", ctypes.c_int32)]
 
 
 _lib = None
@@ -89,8 +90,8 @@ def make_dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
     return Dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv)
 
 
-def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0):
-    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity))
+def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0, max_rule=0):
+    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity), int(max_rule))
 
 
 def _ptr(t):
@@ -259,20 +260,22 @@ def stats_shape(dims, kv_tile):
 
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
-                  out=None, workspace=None, tile_stats=None, stream=None, q16=None, kv_capacity=0):
+                  out=None, workspace=None, tile_stats=None, stream=None, q16=None, kv_capacity=0,
+                  max_rule=MAX_CEIL):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
 
     ``q16=(q, s)`` or ``(q, s, rope_cos, rope_sin)``: take FP16 Q (before RoPE when the tables are
     given) and the Smooth-QK scales (device tensor or None) instead of qkv's Q-hat and quantize Q
     inside the kernel (hifa4_attention_fwd_q16); qkv then needs only the K-hat and V-hat entries.
     ``kv_capacity``: the key rows allocated per (batch, KV head) when qkv's K-hat / V-hat live in a
-    cache (make_cache / cache_append); 0 = Lk.
+    cache (make_cache / cache_append); 0 = Lk.  ``max_rule``: MAX_CEIL (the method) or MAX_NEAREST16
+    (round-to-nearest running max, an accuracy variant; prefill, P-Reordered, no tile statistics).
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
     """
     import torch
-    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity)
+    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule)
     dev = qkv["k_codes"].device
     if out is None:
         out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16, device=dev)

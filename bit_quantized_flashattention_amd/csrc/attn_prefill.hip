@@ -407,7 +407,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
       }
       const float rmax = group_max4(bmax);
       // ---- integer running max, FP16 rescale factor, P-hat scale of this row and tile
-      const RowStep rs = row_step(rmax, m, C);
+      RowStep rs;
+      if constexpr (MODE == 2) rs = row_step_nearest16(rmax, m, C);
+      else rs = row_step(rmax, m, C);
       uint32_t p16[16];
       const uint4 ph = phat_codes(s, C, rs.neg_big_m, p16);
       const uint32_t psc = (uint32_t)(int)(rs.e + 127.0f);
@@ -513,6 +515,8 @@ hipError_t launch4(AttnArgs a, hipStream_t s) {
 template <int D, bool CAUSAL>
 hipError_t launch2(const AttnArgs& a, hipStream_t s) {
   const bool stats = a.stats != nullptr;
+  // the round-to-nearest running max (accuracy variant): P-Reordered, no tile statistics
+  if (a.max_rule == 1) return launch4<D, CAUSAL, 2, false>(a, s);
   if (a.normalizer == 1) return stats ? launch4<D, CAUSAL, 1, true>(a, s) : launch4<D, CAUSAL, 1, false>(a, s);
   return stats ? launch4<D, CAUSAL, 0, true>(a, s) : launch4<D, CAUSAL, 0, false>(a, s);
 }

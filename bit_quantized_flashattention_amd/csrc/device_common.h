@@ -260,6 +260,22 @@ __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   return r;
 }
 
+// The same step under the round-to-nearest running max (an accuracy variant, not the method's
+// reading): m_new = max(m, rn16(fp32(max S * C))), an FP16 value; alpha = rn16(2^rn16(fp32(m -
+// m_new))) from v_exp_f16 (correctly rounded; 0 while m = -inf, and below 2^-30 where rn16
+// gives 0 anyway); m_new + e is rounded once to FP32.
+__device__ __forceinline__ RowStep row_step_nearest16(float rmax, float m, float C) {
+  RowStep r;
+  r.m_new = max_nn(m, (float)(_Float16)(rmax * C));
+  const float d = m - r.m_new;
+  const uint32_t a2 = exp2_h2(pack_h2(d, d));
+  r.alpha = d >= -30.0f ? __builtin_bit_cast(h2, a2)[0] : (_Float16)0.0f;
+  const float mm = max_nn(r.m_new, -0x1p100f);
+  r.e = tile_exponent(__builtin_fmaf(rmax, C, -mm));
+  r.neg_big_m = -(mm + r.e);
+  return r;
+}
+
 // Key and channel maps of the 16x16x128 MFMAs (all offsets inside one 128-key tile).
 //
 // Scores are computed transposed, S^T = K-hat Q-hat^T, with the 16 MFMA columns = 16 queries.

@@ -93,6 +93,8 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
   if (o->normalizer != HIFA4_P_REORDERED && o->normalizer != HIFA4_INCONSISTENT)
     return fail(HIFA4_ERR_SHAPE, "normalizer must be HIFA4_P_REORDERED or HIFA4_INCONSISTENT");
   if (o->kv_tile != 64 && o->kv_tile != 128) return fail(HIFA4_ERR_UNSUPPORTED, "kv_tile must be 64 or 128");
+  if (o->max_rule != HIFA4_MAX_CEIL && o->max_rule != HIFA4_MAX_NEAREST16)
+    return fail(HIFA4_ERR_SHAPE, "max_rule must be HIFA4_MAX_CEIL or HIFA4_MAX_NEAREST16");
   if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
   if (o->kv_capacity != 0 &&
@@ -348,9 +350,16 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
   a.n_tiles = (int32_t)((dims->len_kv + opts->kv_tile - 1) / opts->kv_tile);
   a.causal = opts->causal;
   a.normalizer = opts->normalizer;
+  a.max_rule = opts->max_rule;
   a.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
   hipStream_t stream = (hipStream_t)hip_stream;
   hipError_t e;
+  if (a.max_rule == HIFA4_MAX_NEAREST16) {
+    if (dims->len_q == 1)
+      return fail(HIFA4_ERR_UNSUPPORTED, "attention: HIFA4_MAX_NEAREST16 is prefill-only (the split merge assumes integer maxima)");
+    if (a.stats || a.normalizer != HIFA4_P_REORDERED)
+      return fail(HIFA4_ERR_UNSUPPORTED, "attention: HIFA4_MAX_NEAREST16 runs P-Reordered without tile statistics");
+  }
   if (dims->len_q == 1) {
     if (a.stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
     const size_t need = hifa4_attention_workspace_bytes(dims, opts);

@@ -54,6 +54,7 @@ struct AttnArgs {
   int32_t n_tiles;      // ceil(Lk / kv_tile)
   int32_t causal;
   int32_t normalizer;
+  int32_t max_rule;     // 0: integer running max (the method's reading); 1: round-to-nearest FP16 (prefill)
   int32_t num_splits;
   int32_t tiles_per_split;
   int32_t heads_per_wg;  // prefill: query heads served by one work-group (set by the launcher)

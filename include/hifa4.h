@@ -69,6 +69,14 @@ typedef struct {
 
 enum { HIFA4_P_REORDERED = 0, HIFA4_INCONSISTENT = 1 };
 
+/* Running-max rules.  HIFA4_MAX_CEIL is the method as this library reads the HiFA4 abstract's
+   FP16 online-softmax state: m = max over tiles of ceil(fp32(max S * C)), an integer, so every
+   rescale 2^(m_old - m_new) is an exact power of two.  HIFA4_MAX_NEAREST16 is an accuracy
+   variant: m = max over tiles of rn16(fp32(max S * C)), the rescale alpha = rn16(2^rn16(fp32(
+   m_old - m_new))), and m + e (below) is rounded once to FP32; prefill, P-Reordered, without
+   tile statistics. */
+enum { HIFA4_MAX_CEIL = 0, HIFA4_MAX_NEAREST16 = 1 };
+
 typedef struct {
   int32_t causal;     /* 0 or 1 */
   int32_t normalizer; /* HIFA4_P_REORDERED: l from P-hat (the method); HIFA4_INCONSISTENT: l from
@@ -82,6 +90,7 @@ typedef struct {
                           (a cache filled by hifa4_cache_append); 0 = Lk.  The layouts above then
                           hold with Lk (Lk32) replaced by kv_capacity (rounded up to 32) for the
                           strides, while Lk keys are attended */
+  int32_t max_rule;    /* HIFA4_MAX_CEIL (0) or HIFA4_MAX_NEAREST16 (1, prefill only) */
 } hifa4_attn_opts;
 
 /*
@@ -192,6 +201,8 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * tile_stats: NULL, or FP32 [B, Hq, ceil(Lq/16), ceil(Lk/kv_tile), 2] receiving, per block of 16
  * query rows and key tile, (sum of P-hat, sum of P-tilde) over visible entries (zeros for tiles
  * a row block never visits); prefill only.
+ * Under opts->max_rule = HIFA4_MAX_NEAREST16 the running max and the rescale follow that rule
+ * (see the enum); Lq == 1, INCONSISTENT or tile_stats then return HIFA4_ERR_UNSUPPORTED.
  * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE, HIFA4_ERR_UNSUPPORTED, HIFA4_ERR_WORKSPACE,
  * HIFA4_ERR_ALIGNMENT, HIFA4_ERR_HIP.
  */

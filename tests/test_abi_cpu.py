@@ -100,6 +100,25 @@ def test_attention_rejects_bad_arguments_without_launching(L):
     assert L.hifa4_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(opts)) == 0
 
 
+def test_max_rule_is_validated_and_limited_to_prefill(L):
+    # hifa4_attn_opts: four int32, the int64 capacity at offset 16, max_rule at 24, padded to 32
+    assert ctypes.sizeof(hf.Opts) == 32 and hf.Opts.max_rule.offset == 24
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    pre = hf.make_dims(1, 4, 2, 128, 64, 64)
+    st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(hf.make_opts(max_rule=2)), *([dummy] * 7), None, 0, None, None)
+    assert st == 2 and b"max_rule" in L.hifa4_last_error()
+    near = hf.make_opts(causal=True, max_rule=hf.MAX_NEAREST16)
+    dec = hf.make_dims(2, 8, 2, 128, 1, 4096)
+    st = L.hifa4_attention_fwd(ctypes.byref(dec), ctypes.byref(near), *([dummy] * 7), dummy, 1 << 30, None, None)
+    assert st == 3 and b"prefill-only" in L.hifa4_last_error()
+    inc = hf.make_opts(causal=True, normalizer=hf.INCONSISTENT, max_rule=hf.MAX_NEAREST16)
+    st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(inc), *([dummy] * 7), None, 0, None, None)
+    assert st == 3
+    stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
+    st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(near), *([dummy] * 7), None, 0, stats, None)
+    assert st == 3 and b"statistics" in L.hifa4_last_error()
+
+
 def test_size_limits_are_rejected(L):
     dummy = ctypes.c_void_p(256)
     o = hf.make_opts(causal=False)

@@ -6,11 +6,12 @@ factor; the abstract measures the per-tile error epsilon = sum(P-hat)/sum(P) - 1
 probability-mass loss, and contrasts HiFA4 with direct 4-bit quantization.  This test runs the
 full workload through the C ABI, P-Reordered and inconsistent with per-(16-row block, tile)
 statistics, plus the same two without Smooth-QK (no smoothing + inconsistent is the direct
-formulation) and HiFA4 with the OCP floor block-scale rule, and reports:
+formulation), HiFA4 with the OCP floor block-scale rule and HiFA4 with the round-to-nearest FP16
+running max, and reports:
 
 * epsilon over all visited tiles (median, mean, p5, p95, fraction below 0); m does not depend on
   l, so both runs must produce identical tile sums;
-* the error of the five outputs against unquantized FP32 softmax attention
+* the error of the six outputs against unquantized FP32 softmax attention
   (oracle.reference_fp32 on the original FP16 inputs) on sampled heads.
 
 The magnitude of epsilon has no value on the pages for synthetic inputs (parity unpinned); the
@@ -82,7 +83,12 @@ def test_accuracy_report_batched_prefill():
     runs["floor_scale_rule"] = (hf.attention_fwd(res_floor, dims, True, A.P_REORDERED, cfg["kv_tile"]), None)
     torch.cuda.synchronize()
     del res_floor
-    err = {"p_reordered": [], "inconsistent": [], "no_smooth_p_reordered": [], "direct": [], "floor_scale_rule": []}
+    # the round-to-nearest FP16 running max in place of the integer one (same codes)
+    runs["nearest_running_max"] = (hf.attention_fwd(res, dims, True, A.P_REORDERED, cfg["kv_tile"],
+                                                    max_rule=hf.MAX_NEAREST16), None)
+    torch.cuda.synchronize()
+    err = {"p_reordered": [], "inconsistent": [], "no_smooth_p_reordered": [], "direct": [], "floor_scale_rule": [],
+           "nearest_running_max": []}
     heads = [(0, 0), (2, 9), (5, 22), (7, 31)]
     group = hq // hkv
     for (b, h) in heads:

@@ -195,3 +195,23 @@ def test_floor_scale_rule_saturation_and_attention():
     out = hf.attention_fwd(res, dims, True, 0, 64)
     torch.cuda.synchronize()
     compare_out(out.cpu().numpy(), A.attention_p(qq, True, 64, 0), "floor-rule")
+
+
+@pytest.mark.parametrize("cfg_id,b,hq,hkv,lq,lk,d,causal,kv_tile", [
+    (0, 1, 2, 2, 128, 128, 64, False, 64),     # the tiny non-causal workload
+    (1, 1, 8, 2, 300, 300, 128, True, 128),    # Qwen-shaped, reduced
+    (1, 3, 6, 3, 17, 129, 128, True, 64),      # ragged: a key past a tile, rows past a 16-row block
+    (1, 1, 4, 1, 77, 333, 128, True, 128),     # causal with Lq < Lk
+    (3, 1, 4, 2, 200, 200, 256, True, 128),    # Gemma-shaped d = 256
+    (1, 1, 16, 1, 64, 96, 64, False, 64),      # GQA group of 16, d = 64
+])
+def test_round_to_nearest_running_max(cfg_id, b, hq, hkv, lq, lk, d, causal, kv_tile):
+    """Accuracy variant HIFA4_MAX_NEAREST16: m is the FP16 value nearest to fp32(max S * C) and the
+    rescale the FP16 exp2 of the difference; against the oracle's variant (both entry points)."""
+    cfg, q, k, v, cal = gen(cfg_id, B=b, Hq=hq, Hkv=hkv, Lq=lq, Lk=lk, d=d)
+    print("case nearest max", cfg_id, b, hq, hkv, lq, lk, d, causal, kv_tile, flush=True)
+    got, want, *_ = run_case(q, k, v, causal, kv_tile, calib=cal, alpha=cfg["alpha"], max_rule=A.MAX_NEAREST16)
+    compare_out(got, want, "nearest-max-%d-%d-%d" % (lq, lk, d))
+    # the variant is a different function of the same codes: it must differ from the method's output
+    _, want_ceil, *_ = run_case(q, k, v, causal, kv_tile, calib=cal, alpha=cfg["alpha"])
+    assert np.count_nonzero(want_ceil.view(np.uint16) != want.view(np.uint16)) > 0
