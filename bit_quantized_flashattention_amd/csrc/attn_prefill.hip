@@ -164,20 +164,41 @@ __device__ __forceinline__ void dma(const v4i& desc, uint32_t lds, int voff) {
                  : "m0");
 }
 
-// Issue this wave's n loads of the tile starting at key k0 into the stage at LDS address stage.
+// Section of stage load i (0 K-hat codes, 1 V-hat codes, 2 K-hat scales, 3 V-hat scales, 4 none).
 template <int D>
+constexpr int load_section(int i) {
+  using C = Cfg<D>;
+  return i < C::kKCInstr ? 0 : i < C::kKCInstr + C::kVCInstr ? 1 : i < C::kKCInstr + C::kVCInstr + C::kKSInstr ? 2 : i < C::kInstr ? 3 : 4;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_one(const Slices& sl, int sec, uint32_t dst, int voff, int k0) {
+  using C = Cfg<D>;
+  if (sec == 0) dma<16>(sl.r[0], dst, voff + k0 * C::kKRow);
+  else if (sec == 1) dma<16>(sl.r[1], dst, voff + k0 * C::kKRow);
+  else if (sec == 2) dma<4>(sl.r[2], dst, voff + k0);
+  else dma<4>(sl.r[3], dst, voff + (k0 / kBlock) * D);
+}
+
+// Issue this wave's n loads of the tile starting at key k0 into the stage at LDS address stage.
+// Load i of every wave is stage load wave + W i; where all waves' loads i fall in one section,
+// that section is known at compile time and the load needs no branch.
+template <int D, int I = 0>
 __device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, int n, uint32_t stage, int k0) {
   using C = Cfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::kMaxLoadsPerWave; i++) {
-    if (i >= n) break;
-    const LoadOp& op = ops[i];
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);  // uniform: m0
-    // the whole offset goes in the per-lane operand, which is what the range check covers
-    if (op.sec == 0) dma<16>(sl.r[0], dst, op.voff + k0 * C::kKRow);
-    else if (op.sec == 1) dma<16>(sl.r[1], dst, op.voff + k0 * C::kKRow);
-    else if (op.sec == 2) dma<4>(sl.r[2], dst, op.voff + k0);
-    else dma<4>(sl.r[3], dst, op.voff + (k0 / kBlock) * D);
+  constexpr int W = C::kWaves;
+  if constexpr (I < C::kMaxLoadsPerWave) {
+    const LoadOp& op = ops[I];
+    constexpr int s_lo = load_section<D>(W * I), s_hi = load_section<D>(W * I + W - 1);
+    if constexpr (s_lo == s_hi && s_lo < 4) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);  // uniform: m0
+      issue_one<D>(sl, s_lo, dst, op.voff, k0);
+    } else {
+      if (I >= n) return;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);
+      issue_one<D>(sl, op.sec, dst, op.voff, k0);
+    }
+    issue_tile<D, I + 1>(sl, ops, n, stage, k0);
   }
 }
 
