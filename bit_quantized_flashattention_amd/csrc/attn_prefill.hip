@@ -164,11 +164,20 @@ __device__ __forceinline__ void dma(const v4i& desc, uint32_t lds, int voff) {
                  : "m0");
 }
 
-// Section of stage load i (0 K-hat codes, 1 V-hat codes, 2 K-hat scales, 3 V-hat scales, 4 none).
+// Section of stage load i (0 K-hat codes, 1 V-hat codes, 2 K-hat scales, 3 V-hat scales, 4 none)
+// and its byte offset inside the stage: code loads fill 1 KB each, scale loads 256 bytes.
 template <int D>
-constexpr int load_section(int i) {
+__host__ __device__ constexpr int load_section(int i) {
   using C = Cfg<D>;
   return i < C::kKCInstr ? 0 : i < C::kKCInstr + C::kVCInstr ? 1 : i < C::kKCInstr + C::kVCInstr + C::kKSInstr ? 2 : i < C::kInstr ? 3 : 4;
+}
+template <int D>
+__device__ __forceinline__ int load_lds(int i) {
+  using C = Cfg<D>;
+  if (i < C::kKCInstr) return C::kKC + i * 1024;
+  if (i < C::kKCInstr + C::kVCInstr) return C::kVC + (i - C::kKCInstr) * 1024;
+  if (i < C::kKCInstr + C::kVCInstr + C::kKSInstr) return C::kKS + (i - C::kKCInstr - C::kVCInstr) * 256;
+  return C::kVS + (i - C::kKCInstr - C::kVCInstr - C::kKSInstr) * 256;
 }
 
 template <int D>
@@ -181,24 +190,24 @@ __device__ __forceinline__ void issue_one(const Slices& sl, int sec, uint32_t ds
 }
 
 // Issue this wave's n loads of the tile starting at key k0 into the stage at LDS address stage.
-// Load i of every wave is stage load wave + W i; where all waves' loads i fall in one section,
-// that section is known at compile time and the load needs no branch.
+// Load I of wave w is stage load w + W I; where all waves' loads I fall in one section, that
+// section is known at compile time and the load needs no branch.  LDS addresses are computed
+// from the (scalar) wave index, so they need no vector work.
 template <int D, int I = 0>
-__device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, int n, uint32_t stage, int k0) {
+__device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, int wave_u, int n, uint32_t stage,
+                                           int k0) {
   using C = Cfg<D>;
   constexpr int W = C::kWaves;
   if constexpr (I < C::kMaxLoadsPerWave) {
-    const LoadOp& op = ops[I];
+    const int j = wave_u + W * I;
     constexpr int s_lo = load_section<D>(W * I), s_hi = load_section<D>(W * I + W - 1);
     if constexpr (s_lo == s_hi && s_lo < 4) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);  // uniform: m0
-      issue_one<D>(sl, s_lo, dst, op.voff, k0);
+      issue_one<D>(sl, s_lo, stage + load_lds<D>(j), ops[I].voff, k0);
     } else {
       if (I >= n) return;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + op.lds);
-      issue_one<D>(sl, op.sec, dst, op.voff, k0);
+      issue_one<D>(sl, load_section<D>(j), stage + load_lds<D>(j), ops[I].voff, k0);
     }
-    issue_tile<D, I + 1>(sl, ops, n, stage, k0);
+    issue_tile<D, I + 1>(sl, ops, wave_u, n, stage, k0);
   }
 }
 
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   // prologue: tiles 0 .. kStages-2 in flight, wait for tile 0
 #pragma unroll
   for (int p = 0; p < kStages - 1; p++)
-    if (p < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
+    if (p < n_tiles) issue_tile<D>(sl, ops, wave_u, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
   if (fused_q) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
     const int k0 = tile * bc;
     const uint8_t* T = smem + (tile % kStages) * Cf::kStageBytes;
     const int ahead = tile + kStages - 1;
-    if (ahead < n_tiles) issue_tile<D>(sl, ops, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
+    if (ahead < n_tiles) issue_tile<D>(sl, ops, wave_u, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
 
     if (wave_live && !(CAUSAL && k0 > wave_last + shift)) {
       // ---- S^T = K-hat Q-hat^T: MFMA t takes key score_row_key(t, r) as row r; its operands sit
