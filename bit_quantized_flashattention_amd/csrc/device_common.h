@@ -355,11 +355,13 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
 // the exact residual fma(-l, q, x), which leaves q within 0.5 ulp (FP32) plus O(2^-45) of x / l;
 // a quotient of two FP16 values is never an FP16 rounding midpoint (a midpoint has 12
 // significant bits) and stays at least 2^-22 (relative) away from one, so both round to the same
-// FP16 value.  The sign is copied from x (the quotient of -0 is -0).
+// FP16 value.  The residual is taken negated, d = fma(l, q, -x) (the same rounding of the same
+// exact value with the opposite sign), and the correction is q - d r: then x = -0 keeps its sign
+// through every step (q = -0, d = +0, -0 * r + -0 = -0) without a separate sign copy.
 __device__ __forceinline__ float quot_h(float x, float l, float r) {
   const float q = x * r;
-  const float e = __builtin_fmaf(-l, q, x);
-  return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
+  const float d = __builtin_fmaf(l, q, -x);
+  return __builtin_fmaf(-d, r, q);
 }
 
 template <int CB>
