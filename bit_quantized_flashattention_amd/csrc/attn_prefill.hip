@@ -7,11 +7,12 @@
 // Work decomposition.  A work-group serves one (batch, KV head) and BQ query positions of each
 // of HW query heads of the GQA group; every K-hat/V-hat tile staged in LDS is shared by all of
 // its waves.  A wave owns one block of 16 query rows of one head, the column block of the
-// 16x16x128 scaled FP4 MFMA, so its registers hold one score tile at a time: 16 waves per
-// work-group (4 per SIMD) for d <= 128 and 8 for d = 256, enough waves per SIMD for one wave's
-// exponentials to run while another waits on its matrix products or LDS reads.  Tiles are
-// double-buffered: the next tile is fetched from HBM into registers while the current one is
-// computed, so one barrier per tile remains.
+// 16x16x128 scaled FP4 MFMA, so its registers hold one score tile at a time.  A work-group has 8
+// waves; with registers capped at 80 (d <= 128) three work-groups share a CU, 6 waves per SIMD
+// (4 at d = 256), enough for one wave's exponentials to run while another waits on its matrix
+// products or LDS reads.  Tiles are double-buffered in LDS: the next tile is copied from HBM
+// straight into LDS (buffer loads that write LDS) while the current one is computed, so one
+// barrier per tile remains.
 //
 // Layout trick.  Scores are computed transposed, S^T = K-hat Q-hat^T, so a query is an MFMA
 // column and lives in lanes (l % 16) of all four 16-lane groups.  MFMA t (t = 0..7) takes key
