@@ -151,6 +151,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // HBM -> LDS without registers: each lane's SIZE bytes at voff (+ the descriptor's base) land at
 // LDS address m0 + lane * SIZE.  The load is tracked by the wave's vector-memory counter only;
 // the kernel waits for it explicitly (wait_vmem) before the barrier that publishes the stage.
+// It is written as inline assembly on purpose: with the compiler's buffer-to-LDS builtin the
+// compiler cannot tell the stages apart and puts a wait for every outstanding load (the next
+// tile's included) before the first LDS read of the current tile, which removes the overlap of
+// loading and computing.  m0 is set inside the statement; the compiler uses m0 for nothing else
+// in these kernels (checked in the generated code), so the clobber is safe.
 template <int SIZE>
 __device__ __forceinline__ void dma(const v4i& desc, uint32_t lds, int voff) {
   if (SIZE == 16)
