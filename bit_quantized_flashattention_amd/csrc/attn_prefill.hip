@@ -263,11 +263,20 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   const int wph = W / hw;         // waves per head
   const int bq = 16 * wph;        // query positions per head per work-group
   const int chunks = group / hw;
-  const int kvh = blockIdx.y / chunks;
-  const int h = kvh * group + (blockIdx.y % chunks) * hw + wave / wph;
-  const int b = blockIdx.z;
+  // XCD-aware order: the hardware deals work-groups round-robin over the 8 XCDs, so hardware
+  // index i runs on XCD i % 8.  Renumbering gives each XCD a contiguous range of logical
+  // work-groups (x fastest: the query blocks of one (batch, KV head) together), so the K-hat /
+  // V-hat tiles those work-groups share stay in that XCD's L2.
+  const uint32_t nwg = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t hwid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const uint32_t per = nwg / 8, rem = nwg % 8, xcd = hwid % 8;
+  const uint32_t lin = xcd * per + (xcd < rem ? xcd : rem) + hwid / 8;
+  const uint32_t bx = lin % gridDim.x, by = (lin / gridDim.x) % gridDim.y, bz = lin / (gridDim.x * gridDim.y);
+  const int kvh = by / chunks;
+  const int h = kvh * group + (by % chunks) * hw + wave / wph;
+  const int b = bz;
   // heaviest causal blocks first: they start while the short ones fill the tail
-  const int qblk = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int qblk = CAUSAL ? (int)(gridDim.x - 1 - bx) : (int)bx;
   const int lq = (int)a.len_q, lk = (int)a.len_kv, lk32 = (int)a.len_kv32;
   const int64_t rows = a.kv_rows, rows32 = a.kv_rows32;  // strides of the K-hat / V-hat buffers
   const int q_wg = qblk * bq;
