@@ -254,7 +254,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-derived values stay scalar
+  const int wave = tid >> 6;
   const int g = lane >> 4;    // lane group: K-chunk of the MFMA operands / key block of P-hat
   const int col = lane & 15;  // MFMA column: query within the wave's 16-row block
 
