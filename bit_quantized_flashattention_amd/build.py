@@ -26,9 +26,34 @@ FLAGS = [
 ]
 
 
+def kernel_spills(remarks):
+    """(kernel, VGPR spills, scratch bytes per lane) for every kernel of a compile's
+    kernel-resource-usage remarks that spills or uses scratch."""
+    out = []
+    name = None
+    spill = scratch = 0
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].split("[-Rpass")[0].strip()
+        if text.startswith("Function Name:"):
+            if name is not None and (spill or scratch):
+                out.append((name, spill, scratch))
+            name, spill, scratch = text.split(":", 1)[1].strip(), 0, 0
+        elif text.startswith("VGPRs Spill:"):
+            spill = int(text.split(":", 1)[1])
+        elif text.startswith("ScratchSize [bytes/lane]:"):
+            scratch = int(text.split(":", 1)[1])
+    if name is not None and (spill or scratch):
+        out.append((name, spill, scratch))
+    return out
+
+
 def _compile(src):
     obj = os.path.join(OBJDIR, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    # the resource remarks report register spills, which cost the kernels far more than the
+    # registers they save (a spilling loop also waits on its in-flight tile loads)
+    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):  # host-only C++: the HIP runtime API, no device code
         cmd = [HIPCC, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-D__HIP_PLATFORM_AMD__",
                "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -36,6 +61,8 @@ def _compile(src):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    for name, spill, scratch in kernel_spills(r.stderr):
+        print("warning: %s spills %d VGPRs (%d scratch bytes per lane)" % (name, spill, scratch), file=sys.stderr)
     return obj
 
 
