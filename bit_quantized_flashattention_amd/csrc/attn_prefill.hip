@@ -267,11 +267,13 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   // index i runs on XCD i % 8.  Renumbering gives each XCD a contiguous range of logical
   // work-groups (x fastest: the query blocks of one (batch, KV head) together), so the K-hat /
   // V-hat tiles those work-groups share stay in that XCD's L2.
-  const uint32_t nwg = gridDim.x * gridDim.y * gridDim.z;
-  const uint32_t hwid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const uint32_t per = nwg / 8, rem = nwg % 8, xcd = hwid % 8;
-  const uint32_t lin = xcd * per + (xcd < rem ? xcd : rem) + hwid / 8;
-  const uint32_t bx = lin % gridDim.x, by = (lin / gridDim.x) % gridDim.y, bz = lin / (gridDim.x * gridDim.y);
+  // (64-bit: the grid's three dimensions may multiply past 2^32)
+  const uint64_t gx = gridDim.x, gy = gridDim.y;
+  const uint64_t nwg = gx * gy * gridDim.z;
+  const uint64_t hwid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint64_t per = nwg / 8, rem = nwg % 8, xcd = hwid % 8;
+  const uint64_t lin = xcd * per + (xcd < rem ? xcd : rem) + hwid / 8;
+  const uint32_t bx = (uint32_t)(lin % gx), by = (uint32_t)((lin / gx) % gy), bz = (uint32_t)(lin / (gx * gy));
   const int kvh = by / chunks;
   const int h = kvh * group + (by % chunks) * hw + wave / wph;
   const int b = bz;
