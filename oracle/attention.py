@@ -18,20 +18,30 @@ Readings where the pages are silent (each is listed in the design notes):
   rescale alpha = 2**(m_old - m_new) is exact and m is exact in FP16;
 * the softmax runs on FP16 values, as the FP16 online-softmax state suggests:
   P-tilde = 2**e * rn16(2**rn16(u)) with u = fma32(S, C, -(m + e)), i.e. the
-  log2-domain score, taken relative to the tile's scale 2**e, is rounded to
-  FP16 and exponentiated to a correctly rounded FP16 value;
-* P-hat ("each probability tile is quantized"): E2M1 codes with one power-of-two
-  scale 2**e per (query row, key tile); e is the smallest exponent that keeps
-  the row's largest probability in the tile inside the E2M1 range without
-  clipping, e = ceil(fp32(v - L6)) with v = fma32(max S, C, -m) and
-  L6 = fp32(log2 6), clamped to [-127, 127]; the codes are the round-to-
-  nearest-even E2M1 values of the FP16 probabilities rn16(2**rn16(u)) (the
-  decision idea follows the FP4 attention prior art [FA4P], which maps scores
-  straight to FP4 probabilities).  A tile-level scale flushes probabilities
-  below ~1/16 of the tile maximum to zero, the net probability-mass loss the
-  abstract reports for every tile; it also keeps every sum of the fused
-  P-hat [V-hat | 1] product within 24 bits when V-hat's block scales are
-  close, so the matrix instruction's result is exact;
+  log2-domain score, taken relative to the scale 2**e of its block, is rounded
+  to FP16 and exponentiated to a correctly rounded FP16 value;
+* P-hat is the 4-bit operand of the PV product ([HiFA4] Abstract), so it takes
+  the library's 4-bit format: E2M1 codes with one power-of-two scale per block
+  of 32 elements along the contraction axis, i.e. one scale 2**e per (query
+  row, 32-key block).  e is the smallest exponent that keeps the block's
+  largest probability inside the E2M1 range without clipping, e = ceil(fp32(v
+  - L6)) with v = fma32(max_block S, C, -m) and L6 = fp32(log2 6), clamped to
+  [-127, 127] (-127 for a block without a visible key); the codes are the
+  round-to-nearest-even E2M1 values of the FP16 probabilities rn16(2**rn16(u));
+* accuracy variant PHAT_TILE (not the method's reading): one scale per (query
+  row, key tile), from the row's largest score in the tile; it flushes every
+  probability below about 1/12 of the tile maximum to zero;
+* code-rule variant PHAT_DIRECT ([FA4P] Abstract: scores are mapped straight to
+  FP4 probabilities, with no exponential): the log2-domain score x = w + delta
+  (w = fma32(S, C, K) with K = fp32(127 - (m + e)) + delta folded in, see
+  ``direct_codes``) is turned into the FP32 value whose exponent field is
+  floor(x) and whose mantissa field is frac(x) -- the piecewise-linear
+  (Mitchell) value 2**floor(x) * (1 + frac(x)) -- and that value is rounded to
+  E2M1.  delta = 1/4 - log2(1.5)/2 places the rounding boundaries of every
+  code of value >= 1 at the midpoints, in the log2 domain, of neighbouring E2M1
+  values (nearest E2M1 value in the log domain); the block exponent is the
+  smallest that keeps the block maximum's value <= 6,
+  e = ceil(fp32(v + fp32(delta - 2.5)));
 * inside a scaled matrix instruction the four 32-element block products are
   each exact and are added to the accumulator in block order, with one FP32
   round-to-nearest-even per addition (``mfma_seq``);
@@ -39,10 +49,10 @@ Readings where the pages are silent (each is listed in the design notes):
   l_new = fma16(alpha, l, rn16(L)) with alpha = rn16(2**(m_old - m_new)) and
   PV, L = rowsum(P-hat) from the same instruction sequence (ones column), so
   O and l follow one rule; out = fp16(fp32(O) / fp32(l));
-* the inconsistent variant sums the FP16 probabilities rn16(2**rn16(u)) in
-  FP32 in a fixed tree order (pairs (k, k+16), (k, k+8), ... inside each
-  32-key block, then (s0 + s1) + (s2 + s3) over the blocks of a 128-key
-  tile) and multiplies the sum by 2**e in FP32;
+* the inconsistent variant sums the FP16 probabilities rn16(2**rn16(u)) of
+  each 32-key block in FP32 in a fixed tree order (pairs (k, k+16), (k, k+8),
+  ...), scales each block sum by its 2**e (exact), and adds the block sums
+  of a 128-key tile as (s0 + s1) + (s2 + s3) in FP32;
 * causal masking is bottom-right aligned: key c is visible to query r iff
   c <= r + (Lk - Lq);
 * split-KV decode: splits cover whole tiles, each split runs the recurrence
@@ -82,6 +92,23 @@ def softmax_scale_log2(d):
 
 LOG2_SIX = F32(math.log2(6.0))  # nearest FP32 to log2(6), pinned in the tests
 
+# P-hat scale granularity: one scale per (query row, 32-key block) is the method's reading (the
+# 4-bit format's block); one per (query row, key tile) is an accuracy variant
+PHAT_BLOCK32 = 0
+PHAT_TILE = 1
+# P-hat code rule: RNE E2M1 of the FP16 probabilities (the method's reading), or Direct-P (codes
+# built straight from the log2-domain score, no exponential; the FA4P prior art)
+PHAT_EXP16 = 0
+PHAT_DIRECT = 1
+
+# Direct-P constants (nearest FP32 values, pinned in the tests): delta = 1/4 - log2(1.5)/2 moves
+# the mantissa-rounding points 1.25 and 1.75 of the linear-mantissa value onto the log2-domain
+# midpoints of neighbouring E2M1 values; delta - 2.5 gives the block exponent (the value
+# 2**floor(x) * (1 + frac(x)) is 6, the largest E2M1 magnitude, at x = 2.5)
+DIRECT_DELTA = F32(0.25 - math.log2(1.5) / 2)
+DIRECT_TOP = F32(0.25 - math.log2(1.5) / 2 - 2.5)
+TWO23 = F32(2.0 ** 23)
+
 
 def tile_exponent(v):
     """P-hat scale exponent of a (row, tile): e = ceil(fp32(v - L6)), clamped to [-127, 127].
@@ -94,6 +121,45 @@ def tile_exponent(v):
         e = np.ceil(t.astype(F64))
     e = np.where(np.isfinite(e), e, -127.0)
     return np.clip(e, -127, 127).astype(np.int64)
+
+
+def direct_exponent(v):
+    """Direct-P block exponent: e = ceil(fp32(v + fp32(delta - 2.5))), clamped to [-127, 127].
+
+    v = fma32(max S, C, -m) is the log2 of the block's largest probability; the block maximum's
+    Direct-P value is then at most 6.
+    """
+    t = fp.add32(np.asarray(v, dtype=F32), DIRECT_TOP)
+    with np.errstate(invalid="ignore"):
+        e = np.ceil(t.astype(F64))
+    e = np.where(np.isfinite(e), e, -127.0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def direct_codes(s, c32, big_m):
+    """Direct-P E2M1 codes of FP32 scores s relative to 2**big_m (big_m = m + e, FP32).
+
+    K = fp32(fp32(127 - big_m) + delta); y = fma32(s, C * 2**23, K * 2**23) = 2**23 *
+    fma32(s, C, K); the integer part of y (0 for y <= 0) read as the bits of an FP32 number is
+    z = 2**floor(x) * (1 + frac(x)) with x = y / 2**23 - 127 (mantissa truncated to 23 bits);
+    the code is the RNE E2M1 code of z (saturating at 6).  Returns (codes, z).
+    """
+    s = np.asarray(s, dtype=F32)
+    k = fp.add32(fp.add32(F32(127.0), -np.asarray(big_m, dtype=F32)), DIRECT_DELTA)
+    y = fp.fma32(s, fp.mul32(c32, TWO23), fp.mul32(k, TWO23)).astype(F64)
+    t = np.where(np.isfinite(y) & (y > 0), np.floor(np.where(np.isfinite(y), y, 0.0)), 0.0)
+    t = np.minimum(t, 2.0 ** 32 - 1).astype(np.uint64).astype(np.uint32)
+    z = t.view(F32)
+    return mx.rne_code(z.astype(F64)), z
+
+
+def mitchell(x):
+    """2**floor(x) * (1 + frac(x)) in FP64: the linear interpolation of 2**x between integers."""
+    x = np.asarray(x, dtype=F64)
+    with np.errstate(invalid="ignore"):
+        fl = np.floor(x)
+        return np.where(np.isfinite(x), np.ldexp(1.0 + (x - np.where(np.isfinite(x), fl, 0.0)),
+                                                 np.where(np.isfinite(x), fl, 0.0).astype(np.int64)), 0.0)
 
 
 def exp2_16(u):
@@ -241,6 +307,40 @@ def _tree_sum32(x):
 # the recurrence
 # ----------------------------------------------------------------------------------------------
 
+def phat_tile(st, vt, c32, mm, nb, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
+    """P-hat of one key tile at Level P.
+
+    st FP32 scores [R, bc], vt visibility [R, bc], mm FP32 [R] running max after this tile
+    (any finite stand-in for a row without a visible key), nb = bc / 32.  Returns the codes
+    [R, bc] (0 where not visible), the scale exponents [R, nb] (one per 32-key block; under
+    PHAT_TILE all blocks of a row share the row's) and the FP16 probabilities
+    rn16(2**rn16(fma32(S, C, -(m + e)))) [R, bc] (None under PHAT_DIRECT).
+    """
+    r_n, bc = st.shape
+    sv = np.where(vt, st, F32(-np.inf)).reshape(r_n, nb, 32)
+    bvis = vt.reshape(r_n, nb, 32).any(axis=2)
+    if phat_scale == PHAT_TILE:
+        anyv = bvis.any(axis=1)
+        top = np.where(anyv, sv.max(axis=(1, 2)), F32(0)).astype(F32)
+        e_row = np.where(anyv, tile_exponent(fp.fma32(top, c32, -mm)), -127)
+        eb = np.repeat(e_row[:, None], nb, axis=1)
+    else:
+        top = np.where(bvis, sv.max(axis=2), F32(0)).astype(F32)
+        v = fp.fma32(top, c32, -mm[:, None])
+        rule = direct_exponent if phat_rule == PHAT_DIRECT else tile_exponent
+        eb = np.where(bvis, rule(v), -127)
+    big_m = np.repeat(fp.add32(mm[:, None], eb.astype(F32)), 32, axis=1)  # exact for integer m
+    s0 = np.where(vt, st, F32(0))
+    if phat_rule == PHAT_DIRECT:
+        codes, _ = direct_codes(s0, c32, big_m)
+        p16 = None
+    else:
+        u = fp.fma32(s0, c32, -big_m)
+        p16 = np.where(vt, exp2_16(u), np.float16(0))
+        codes = mx.rne_code(p16.astype(F64))
+    return np.where(vt, codes, 0).astype(np.uint8), eb, p16
+
+
 class State:
     def __init__(self, m, l, o):
         self.m, self.l, self.o = m, l, o
@@ -258,7 +358,8 @@ class Diag:
         self.stats = []  # (row_block, tile, sum_phat, sum_p)
 
 
-def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row_ids=None, max_rule=MAX_CEIL):
+def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row_ids=None, max_rule=MAX_CEIL,
+                 phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """Level-P tile loop for one head over tiles [tile_lo, tile_hi).
 
     s fp32 [R, Npad] scores, vis [R, Npad], vh int64 [d, Npad] V-hat codes in
@@ -267,8 +368,12 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
 
     max_rule MAX_NEAREST16 (accuracy variant): m_new = max(m, rn16(fp32(max S * C))), the rescale
     is alpha = rn16(2**rn16(fp32(m - m_new))) (the FP16 exp2 of the FP32 difference), and
-    m_new + e is rounded once to FP32; everything else is as under MAX_CEIL.
+    m_new + e is rounded once to FP32; everything else is as under MAX_CEIL.  phat_scale and
+    phat_rule select P-hat's scale granularity and code rule (see ``phat_tile``); PHAT_DIRECT has
+    no FP16 probabilities, so it runs P_REORDERED without epsilon statistics.
     """
+    if phat_rule == PHAT_DIRECT and (mode != P_REORDERED or row_ids is not None):
+        raise ValueError("Direct-P codes have no FP16 probabilities: P_REORDERED without statistics only")
     r_n = s.shape[0]
     d = vh.shape[0]
     m = np.full(r_n, -np.inf, dtype=F32)
@@ -294,15 +399,7 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
             diff = fp.add32(np.where(fin, m, F32(0)), -np.where(fin, m_new, F32(0)))
             alpha16 = np.where(np.isneginf(m), np.float16(0), exp2_16(diff)).astype(np.float16)
         mm = np.where(np.isfinite(m_new), m_new, F32(0)).astype(F32)
-        # P-hat: one power-of-two scale per (row, tile), from the tile's largest score
-        top = np.where(anyv, smax, F32(0)).astype(F32)
-        e_row = np.where(anyv, tile_exponent(fp.fma32(top, c32, -mm)), -127)
-        big_m = fp.add32(mm, e_row.astype(F32))  # exact for integer m
-        u = fp.fma32(np.where(vt, st, F32(0)), c32, -big_m[:, None])
-        p16 = np.where(vt, exp2_16(u), np.float16(0))
-        codes = np.where(vt, mx.rne_code(p16.astype(F64)), 0).astype(np.uint8)
-        ptil = p16.astype(F64) * np.exp2(e_row.astype(F64))[:, None]  # P-tilde, exact
-        eb = np.repeat(e_row[:, None], nb, axis=1)
+        codes, eb, p16 = phat_tile(st, vt, c32, mm, nb, phat_scale, phat_rule)
         ph = mx.code_half_units(codes)
         pv_blocks = []
         l_blocks = []
@@ -317,10 +414,11 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
         pv, ok_pv = mfma_seq(pv_blocks)
         lsum, ok_l = mfma_seq(l_blocks)
         if mode == INCONSISTENT:
-            sums = [_tree_sum32(p16[:, 32 * j:32 * j + 32].astype(F32)) for j in range(nb)]
+            # each block's FP32 tree sum times its own scale (exact), then (s0 + s1) + (s2 + s3)
+            sums = [fp.mul32(_tree_sum32(p16[:, 32 * j:32 * j + 32].astype(F32)),
+                             np.exp2(eb[:, j].astype(F64)).astype(F32)) for j in range(nb)]
             sums += [np.zeros(r_n, dtype=F32)] * (4 - nb) if nb < 4 else []
-            tree = fp.add32(fp.add32(sums[0], sums[1]), fp.add32(sums[2], sums[3]))
-            lsum = fp.mul32(tree, np.exp2(e_row.astype(F64)).astype(F32))
+            lsum = fp.add32(fp.add32(sums[0], sums[1]), fp.add32(sums[2], sums[3]))
         o16 = fp.fma16(alpha16[:, None], o16, fp.rn16(pv))
         l16 = fp.fma16(alpha16, l16, fp.rn16(lsum))
         m = m_new
@@ -330,7 +428,9 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
             diag.inexact_l += int((~ok_l[rows_touch]).sum())
             diag.total_pv += int(rows_touch.sum()) * d
             if row_ids is not None:
-                phat = mx.code_value(codes) * np.exp2(np.repeat(eb, 32, axis=1).astype(F64))
+                scale = np.exp2(np.repeat(eb, 32, axis=1).astype(F64))
+                phat = mx.code_value(codes) * scale
+                ptil = p16.astype(F64) * scale  # P-tilde, exact
                 for rb in np.unique(np.asarray(row_ids) // STATS_ROWS):
                     sel = (np.asarray(row_ids) // STATS_ROWS) == rb
                     if vt[sel].any():
@@ -339,11 +439,14 @@ def recurrence_p(s, vis, vh, ve, c32, bc, mode, tile_lo, tile_hi, diag=None, row
 
 
 def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True, round_state=True,
-                 max_rule=MAX_CEIL):
+                 max_rule=MAX_CEIL, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """Level-S tile loop: exact scores and exp2, rounding only where a narrow format is stored.
 
     vvals FP64 [Npad, d] (dequantized V-hat, or the raw V for the identity quantizer).  Under
     MAX_NEAREST16 the running max is the FP16 rounding of max S * C (m is stored in FP16).
+    P-hat quantizes the exact probabilities p = 2**(S C - m) with one scale per 32-key block (or
+    per tile under PHAT_TILE); under PHAT_DIRECT the codes are the RNE E2M1 codes of
+    mitchell(log2 p - e + delta) with e = ceil(max log2 p + delta - 2.5).
     """
     r_n = s64.shape[0]
     d = vvals.shape[1]
@@ -362,11 +465,10 @@ def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True
             m_new = np.where(anyv, np.maximum(m, top), m)
             alpha = np.where(m_new == m, 1.0, np.where(np.isneginf(m), 0.0, np.exp2(m - m_new)))
         mm = np.where(np.isfinite(m_new), m_new, 0.0)
-        p = np.where(vt, np.exp2(np.where(vt, st, 0.0) * c64 - mm[:, None]), 0.0)
+        u = np.where(vt, st, 0.0) * c64 - mm[:, None]
+        p = np.where(vt, np.exp2(u), 0.0)
         if quantize:
-            e = mx.scale_exponent(p.max(axis=1))
-            y = p * np.exp2(-e.astype(F64))[:, None]
-            ph = mx.code_value(mx.rne_code(y)) * np.exp2(e.astype(F64))[:, None]
+            ph = _phat_s(u, p, vt, bc // 32, phat_scale, phat_rule)
         else:
             ph = p
         pv = ph @ vvals[k0:k0 + bc]
@@ -378,6 +480,28 @@ def recurrence_s(s64, vis, vvals, c64, bc, mode, tile_lo, tile_hi, quantize=True
             l = l.astype(np.float16).astype(F64)
         m = m_new
     return State(m, l, o)
+
+
+def _phat_s(u, p, vt, nb, phat_scale, phat_rule):
+    """Level-S P-hat values of one tile from the exact log2 probabilities u and p = 2**u."""
+    r_n, bc = p.shape
+    if phat_scale == PHAT_TILE:
+        blocks = p.max(axis=1, keepdims=True)  # one scale per row
+        e = np.repeat(mx.scale_exponent(blocks), nb, axis=1)
+    else:
+        e = mx.scale_exponent(p.reshape(r_n, nb, 32).max(axis=2))
+    ek = np.repeat(e, 32, axis=1).astype(F64)
+    if phat_rule == PHAT_DIRECT:
+        delta = 0.25 - math.log2(1.5) / 2
+        bvis = vt.reshape(r_n, nb, 32).any(axis=2)
+        umax = np.where(vt, u, -np.inf).reshape(r_n, nb, 32).max(axis=2)
+        with np.errstate(invalid="ignore"):
+            e = np.where(bvis, np.ceil(np.where(bvis, umax, 0.0) + delta - 2.5), -127.0)
+        ek = np.repeat(np.clip(e, -127, 127), 32, axis=1)
+        z = np.where(vt, mitchell(np.where(vt, u, 0.0) - ek + delta), 0.0)
+        return mx.code_value(mx.rne_code(z)) * np.exp2(ek)
+    y = p * np.exp2(-ek)
+    return mx.code_value(mx.rne_code(y)) * np.exp2(ek)
 
 
 def finish(state, level="P"):
@@ -417,7 +541,8 @@ def split_tiles(n_tiles, num_splits):
     return [(min(s * per, n_tiles), min((s + 1) * per, n_tiles)) for s in range(num_splits)]
 
 
-def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, stats=False, max_rule=MAX_CEIL):
+def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, stats=False, max_rule=MAX_CEIL,
+                     phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """Level-P output rows of one (batch, query head): FP16 [len(rows), d].
 
     MAX_NEAREST16 is defined for the unsplit (prefill) loop only.
@@ -445,34 +570,37 @@ def attention_head_p(qq, b, h, rows, causal, bc, mode, num_splits=1, diag=None, 
         diag.total_s += int(vis[:, :lk].sum())
     c32 = softmax_scale_log2(d)
     if num_splits <= 1:
-        st = recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, 0, n_tiles, diag, rows if stats else None, max_rule)
+        st = recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, 0, n_tiles, diag, rows if stats else None, max_rule,
+                          phat_scale, phat_rule)
         return finish(st, "P")
     assert max_rule == MAX_CEIL, "the split-KV merge is defined for integer running maxima"
-    states = [recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, lo, hi, diag) for lo, hi in split_tiles(n_tiles, num_splits)]
+    states = [recurrence_p(s_pad, vis, vh, ve, c32, bc, mode, lo, hi, diag, None, MAX_CEIL, phat_scale, phat_rule)
+              for lo, hi in split_tiles(n_tiles, num_splits)]
     return finish(merge_splits(states), "P")
 
 
-def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None, max_rule=MAX_CEIL):
+def attention_p(qq, causal, bc, mode=P_REORDERED, num_splits=1, diag=None, max_rule=MAX_CEIL,
+                phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """Full Level-P output FP16 [B, Hq, Lq, d]."""
     b_n, hq, lq, d = qq.qc.shape
     out = np.zeros((b_n, hq, lq, d), dtype=np.float16)
     for b in range(b_n):
         for h in range(hq):
             out[b, h] = attention_head_p(qq, b, h, np.arange(lq), causal, bc, mode, num_splits, diag,
-                                         max_rule=max_rule)
+                                         max_rule=max_rule, phat_scale=phat_scale, phat_rule=phat_rule)
     return out
 
 
-def tile_stats_p(qq, causal, bc, b, h):
+def tile_stats_p(qq, causal, bc, b, h, phat_scale=PHAT_BLOCK32):
     """Epsilon statistics of one head: list of (row_block_of_16, tile, sum P-hat, sum P-tilde)."""
     diag = Diag()
     lq = qq.qc.shape[2]
-    attention_head_p(qq, b, h, np.arange(lq), causal, bc, P_REORDERED, 1, diag, stats=True)
+    attention_head_p(qq, b, h, np.arange(lq), causal, bc, P_REORDERED, 1, diag, stats=True, phat_scale=phat_scale)
     return diag.stats
 
 
 def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_state=True, num_splits=1,
-                max_rule=MAX_CEIL):
+                max_rule=MAX_CEIL, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """Level-S output for one head from values: qv [Lq, d], kv [Lk, d], vv [Lk, d] (FP64 values).
 
     With quantize=False and round_state=False this is textbook softmax attention.
@@ -488,10 +616,11 @@ def attention_s(qv, kv, vv, causal, bc, mode=P_REORDERED, quantize=True, round_s
     vpad[:lk] = vv
     c64 = math.log2(math.e) / math.sqrt(d)
     if num_splits <= 1:
-        st = recurrence_s(s, vis, vpad, c64, bc, mode, 0, n_tiles, quantize, round_state, max_rule)
+        st = recurrence_s(s, vis, vpad, c64, bc, mode, 0, n_tiles, quantize, round_state, max_rule, phat_scale,
+                          phat_rule)
         return st.o / st.l[:, None] if not round_state else finish(st, "S")
     # split + exact merge (Level S keeps the partials in FP64)
-    parts = [recurrence_s(s, vis, vpad, c64, bc, mode, lo, hi, quantize, round_state, max_rule)
+    parts = [recurrence_s(s, vis, vpad, c64, bc, mode, lo, hi, quantize, round_state, max_rule, phat_scale, phat_rule)
              for lo, hi in split_tiles(n_tiles, num_splits) if hi > lo]
     m = np.max([p.m for p in parts], axis=0)
     o = sum(np.exp2(p.m - m)[:, None] * p.o for p in parts)

@@ -1,4 +1,5 @@
-"""Write tests/golden/regression_c0.json from the oracle alone (config 0, both normalizers).
+"""Write tests/golden/regression_c0.json from the oracle alone (config 0: both normalizers, the
+per-tile P-hat scale variant and the Direct-P code rule).
 
 Usage: python tests/golden/make_golden.py
 """
@@ -32,6 +33,10 @@ def compute():
         out[name] = digest(arr)
     out["out_p_reordered"] = digest(A.attention_p(qq, cfg["causal"], cfg["kv_tile"], A.P_REORDERED))
     out["out_inconsistent"] = digest(A.attention_p(qq, cfg["causal"], cfg["kv_tile"], A.INCONSISTENT))
+    out["out_phat_tile"] = digest(A.attention_p(qq, cfg["causal"], cfg["kv_tile"], A.P_REORDERED,
+                                                phat_scale=A.PHAT_TILE))
+    out["out_direct_p"] = digest(A.attention_p(qq, cfg["causal"], cfg["kv_tile"], A.P_REORDERED,
+                                               phat_rule=A.PHAT_DIRECT))
     return out
 
 

@@ -215,8 +215,25 @@ def test_theorem1_coherent_scaling():
 
 # ---------------------------------------------------------------- independent scalar evaluation
 
-def scalar_attention_p(qq, b, h, causal, bc, mode):
-    """Level P by plain loops over rows, tiles, blocks and elements."""
+def nearest_e2m1_code(y):
+    """RNE code of a magnitude y >= 0 by search over the eight E2M1 values (ties: even code).
+
+    Independent of mx.rne_code: the nearest value wins; at an exact tie the code whose mantissa
+    bit (bit 0) is 0 wins; above 6 the code saturates.
+    """
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    if y >= 6.0:
+        return 7
+    best = min(range(8), key=lambda c: (abs(vals[c] - y), c & 1))
+    return best
+
+
+def scalar_attention_p(qq, b, h, causal, bc, mode, per_tile=False):
+    """Level P by plain loops over rows, tiles, blocks and elements.
+
+    P-hat has one scale per (row, 32-key block), from the block's largest visible score (or one per
+    (row, tile) with per_tile=True, the accuracy variant).
+    """
     from fractions import Fraction as Fr
     from test_oracle_fp import rn_fraction_to_f16
     hq, hkv = qq.qc.shape[1], qq.kc.shape[1]
@@ -224,6 +241,7 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
     lq, d = qq.qc.shape[2], qq.qc.shape[3]
     lk = qq.lk
     c = A.softmax_scale_log2(d)
+    l6 = F32(math.log2(6.0))
     qv = mx.code_half_units(qq.qc[b, h])
     kv = mx.code_half_units(qq.kc[b, g])
     vv = mx.code_half_units(qq.vc[b, g])
@@ -248,29 +266,32 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
             tm = math.ceil(float(F32(float(max(svals.values())) * float(c))))
             m_new = max(m, tm)
             alpha = 0.0 if m == -math.inf else 2.0 ** (m - m_new)
-            # one P-hat scale 2^e for the row in this tile, from the tile's largest score
-            top = max(svals.values())
-            v_top = fp.fma32(top, c, F32(-m_new))
-            e = max(-127, math.ceil(float(F32(F32(v_top) - F32(math.log2(6.0))))))
-            big_m = F32(m_new + e)
+
+            def exponent_of(top):  # smallest e keeping 2^fma32(top, C, -m) inside 6 * 2^e
+                v_top = fp.fma32(top, c, F32(-m_new))
+                return max(-127, math.ceil(float(fp.add32(F32(v_top), -l6))))
+            escale = {}
+            for blk0 in range(t * bc, t * bc + bc, 32):
+                tops = [svals[cc] for cc in keys if (cc >= t * bc if per_tile else blk0 <= cc < blk0 + 32)]
+                escale[blk0] = exponent_of(max(tops)) if tops else -127
             p16 = {}
+            phat = {}
             for cc in keys:
-                u = fp.fma32(svals[cc], c, -big_m)
+                e = escale[t * bc + (cc - t * bc) // 32 * 32]
+                u = fp.fma32(svals[cc], c, F32(-(m_new + e)))
                 p16[cc] = np.float16(math.pow(2.0, float(np.float16(u))))
-            ptil = {cc: float(p16[cc]) * 2.0 ** e for cc in keys}
-            escale = {blk0: e for blk0 in range(t * bc, t * bc + bc, 32)}
-            phat = {cc: int(mx.code_half_units(mx.rne_code(np.array([float(p16[cc])])))[0]) for cc in keys}
+                phat[cc] = 2 * [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][nearest_e2m1_code(float(p16[cc]))]
             pv = np.zeros(d, dtype=F32)
             for ch in range(d):
                 acc = 0.0
                 for blk0 in range(t * bc, t * bc + bc, 32):
-                    i = sum(phat.get(cc, 0) * int(vv[ch, cc]) for cc in range(blk0, blk0 + 32) if cc < vv.shape[1])
+                    i = sum(int(phat.get(cc, 0)) * int(vv[ch, cc]) for cc in range(blk0, blk0 + 32) if cc < vv.shape[1])
                     val = math.ldexp(i, escale[blk0] + int(qq.ve[b, g, ch, blk0 // 32]) - 2) if blk0 // 32 < qq.ve.shape[3] else 0.0
                     acc = float(fp.rn32_sum(acc, val))
                 pv[ch] = acc
             acc = 0.0
             for blk0 in range(t * bc, t * bc + bc, 32):
-                i = sum(2 * phat.get(cc, 0) for cc in range(blk0, blk0 + 32))
+                i = sum(2 * int(phat.get(cc, 0)) for cc in range(blk0, blk0 + 32))
                 acc = float(fp.rn32_sum(acc, math.ldexp(i, escale[blk0] - 2)))
             lsum = F32(acc)
             if mode == A.INCONSISTENT:
@@ -280,8 +301,8 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
                     while len(vals) > 1:
                         h2 = len(vals) // 2
                         vals = [F32(vals[j] + vals[j + h2]) for j in range(h2)]
-                    parts.append(vals[0] if blk0 < t * bc + bc else F32(0))
-                lsum = F32(F32(F32(parts[0] + parts[1]) + F32(parts[2] + parts[3])) * F32(2.0 ** e))
+                    parts.append(F32(vals[0] * F32(2.0 ** escale[blk0])) if blk0 < t * bc + bc else F32(0))
+                lsum = F32(F32(parts[0] + parts[1]) + F32(parts[2] + parts[3]))
             # FP16 state update: one rounding of alpha * O + fp16(PV), exact rationals
             a16 = np.float16(alpha)
             for ch in range(d):
@@ -293,15 +314,18 @@ def scalar_attention_p(qq, b, h, causal, bc, mode):
     return out
 
 
-@pytest.mark.parametrize("mode", [A.P_REORDERED, A.INCONSISTENT])
-def test_scalar_loops_match_vectorized(mode):
+@pytest.mark.parametrize("mode,per_tile", [(A.P_REORDERED, False), (A.INCONSISTENT, False), (A.P_REORDERED, True)])
+def test_scalar_loops_match_vectorized(mode, per_tile):
     rng = np.random.default_rng(13)
-    q, k, v = rand_qkv(rng, 1, 2, 1, 24, 80, 64)
+    q, k, v = rand_qkv(rng, 1, 2, 1, 24, 80, 64, outlier=20.0)
     qq = A.quantize_qkv(q, k, v)
-    vec = A.attention_p(qq, True, 64, mode)
+    vec = A.attention_p(qq, True, 64, mode, phat_scale=A.PHAT_TILE if per_tile else A.PHAT_BLOCK32)
     for h in range(2):
-        sc = scalar_attention_p(qq, 0, h, True, 64, mode)
+        sc = scalar_attention_p(qq, 0, h, True, 64, mode, per_tile)
         assert np.array_equal(sc, vec[0, h])
+    # the two scale granularities give different outputs on these inputs
+    if not per_tile and mode == A.P_REORDERED:
+        assert not np.array_equal(vec, A.attention_p(qq, True, 64, mode, phat_scale=A.PHAT_TILE))
 
 
 # ---------------------------------------------------------------- level P against level S, splits
@@ -322,7 +346,7 @@ def test_level_p_tracks_level_s_on_config0():
         outs = A.attention_s(qv[0, h], kv[0, h], vv[0, h], False, 64)
         delta = np.abs(outs.astype(np.float64) - outp[0, h].astype(np.float64))
         rms = np.sqrt(np.mean(outs.astype(np.float64) ** 2))
-        assert np.mean(delta > 2e-3 * rms) < 0.01
+        assert np.mean(delta > 2e-3 * rms) < 0.02  # per-32-key P-hat blocks: more live codes near a midpoint
         assert delta.max() < 0.1 * np.abs(outs).max()
     assert diag.inexact_s == 0
 
