@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libhifa4.so")
 P_REORDERED = 0
 INCONSISTENT = 1
 MAX_CEIL, MAX_NEAREST16 = 0, 1  # running-max rules (hifa4.h)
+PHAT_BLOCK32, PHAT_TILE = 0, 1  # P-hat scale granularity (hifa4.h)
+PHAT_EXP16, PHAT_DIRECT = 0, 1  # P-hat code rule (hifa4.h)
 
 
 class Dims(ctypes.Structure):
@@ -31,7 +33,8 @@ class Dims(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("normalizer", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64), ("max_rule", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64), ("max_rule", ctypes.c_int32),
+                ("phat_scale", ctypes.c_int32), ("phat_rule", ctypes.c_int32)]
 
 
 _lib = None
@@ -90,8 +93,10 @@ def make_dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
     return Dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv)
 
 
-def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0, max_rule=0):
-    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity), int(max_rule))
+def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0, max_rule=0,
+              phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
+    return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity), int(max_rule),
+                int(phat_scale), int(phat_rule))
 
 
 def _ptr(t):
@@ -261,7 +266,7 @@ def stats_shape(dims, kv_tile):
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
                   out=None, workspace=None, tile_stats=None, stream=None, q16=None, kv_capacity=0,
-                  max_rule=MAX_CEIL):
+                  max_rule=MAX_CEIL, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
 
     ``q16=(q, s)`` or ``(q, s, rope_cos, rope_sin)``: take FP16 Q (before RoPE when the tables are
@@ -270,12 +275,14 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
     ``kv_capacity``: the key rows allocated per (batch, KV head) when qkv's K-hat / V-hat live in a
     cache (make_cache / cache_append); 0 = Lk.  ``max_rule``: MAX_CEIL (the method) or MAX_NEAREST16
     (round-to-nearest running max, an accuracy variant; prefill, P-Reordered, no tile statistics).
+    ``phat_scale``: PHAT_BLOCK32 (the method) or PHAT_TILE; ``phat_rule``: PHAT_EXP16 (the method) or
+    PHAT_DIRECT (Direct-P codes); the variants run P-Reordered without tile statistics.
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
     """
     import torch
-    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule)
+    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule, phat_scale, phat_rule)
     dev = qkv["k_codes"].device
     if out is None:
         out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16, device=dev)

@@ -77,7 +77,9 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
   }
 }
 
-template <int D, int MODE>
+// PH: the P-hat rule, as in the prefill kernel (0 = per 32-key block from the FP16 probabilities,
+// 1 = per tile, 2 = Direct-P codes)
+template <int D, int MODE, int PH>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
   constexpr int CB = D / 16;
@@ -179,17 +181,20 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
       bmax = fmaxf(bmax, s[k]);
     }
     const float rmax = group_max4(bmax);
-    // integer running max, FP16 rescale factor and the P-hat scale of this tile (all four lane
-    // groups hold the same row maximum, so they agree)
+    // integer running max and FP16 rescale factor (all four lane groups hold the same row
+    // maximum, so they agree); the P-hat scale of the lane's own 32-key block
     const RowStep rs = row_step(rmax, m, C);
+    const PhatScale ps = phat_scale<PH == 2>(PH == 1 ? rmax : bmax, C, rs.mm);
     uint32_t p16[16];
-    const uint4 ph = phat_codes(s, C, rs.neg_big_m, p16);
-    const uint32_t psc = (uint32_t)(int)(rs.e + 127.0f);
+    uint4 ph;
+    if constexpr (PH == 2) ph = phat_codes_direct(s, C, ps.neg_big_m);
+    else ph = phat_codes(s, C, ps.neg_big_m, p16);
+    const uint32_t psc = (uint32_t)(int)(ps.e + 127.0f);
     const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
     v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
     lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
     float lsum = lacc[0];
-    if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16)) * e8m0_as_float((int)rs.e);
+    if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16) * e8m0_as_float((int)ps.e));
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
       v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -249,8 +254,10 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int group = a.heads_q / a.heads_kv;
   dim3 grid((uint32_t)a.num_splits, (uint32_t)(a.heads_kv * ((group + 15) / 16)), (uint32_t)a.batch);
-  if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((attn_decode_split_kernel<D, 0>), grid, dim3(64), 0, s, a);
+  if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1, 0>), grid, dim3(64), 0, s, a);
+  else if (a.phat == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 1>), grid, dim3(64), 0, s, a);
+  else if (a.phat == 2) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 2>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 0>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((uint32_t)((int64_t)a.batch * a.heads_q)), dim3(D), 0, s, a);

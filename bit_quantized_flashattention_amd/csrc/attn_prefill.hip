@@ -16,11 +16,12 @@
 //
 // Layout trick.  Scores are computed transposed, S^T = K-hat Q-hat^T, so a query is an MFMA
 // column and lives in lanes (l % 16) of all four 16-lane groups.  MFMA t (t = 0..7) takes key
-// 32*(r/4) + 4t + (r%4) as its row r; its output register i of lane group g then holds key
-// 32g + 4t + i.  After the 8 MFMAs each lane holds the 32 contiguous keys of one 32-key block of
-// its query: exactly the per-lane slice the PV MFMA consumes as its B operand (P-hat^T), so
-// P-hat is quantized and packed in registers without any data exchange; its scale (one per
-// query and tile) needs only the row maximum, two row-swap permutes.  O^T = V-hat^T P-hat^T
+// 32*(r/4) + 8*(r%4) + t as its row r; its output register i of lane group g then holds key
+// 32g + 8i + t.  After the 8 MFMAs each lane holds the 32 keys of one 32-key block of its query:
+// exactly the per-lane slice the PV MFMA consumes as its B operand (P-hat^T), so P-hat is
+// quantized and packed in registers without any data exchange, and its scale (one per query and
+// 32-key block, the PV MFMA's per-lane B scale) comes from the lane's own maximum; the running
+// max needs the row maximum, two row-swap permutes.  O^T = V-hat^T P-hat^T
 // then puts a query's outputs in its own lanes too, so the FP16 state update needs no exchange
 // either.
 //
@@ -244,7 +245,10 @@ __device__ __forceinline__ const float* q_smooth_blk(const AttnArgs& a, int kvh,
   return a.q_smooth != nullptr ? a.q_smooth + (int64_t)kvh * d + c0 : nullptr;
 }
 
-template <int D, bool CAUSAL, int MODE, bool STATS>
+// PH: the P-hat rule: 0 = one scale per (row, 32-key block), codes from the FP16 probabilities
+// (the method); 1 = one scale per (row, tile) (accuracy variant); 2 = Direct-P codes, one scale
+// per (row, 32-key block)
+template <int D, bool CAUSAL, int MODE, bool STATS, int PH>
 __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_MIN_WAVES : 4) void attn_prefill_kernel(AttnArgs a) {
   using Cf = Cfg<D>;
   constexpr int W = Cf::kWaves;
@@ -453,24 +457,28 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
         }
       }
       const float rmax = group_max4(bmax);
-      // ---- integer running max, FP16 rescale factor, P-hat scale of this row and tile
+      // ---- integer running max, FP16 rescale factor; P-hat scale of this lane's block (its own
+      // maximum bmax: the lane holds one 32-key block of its row), or of the row's tile (PH = 1)
       RowStep rs;
       if constexpr (MODE == 2) rs = row_step_nearest16(rmax, m, C);
       else rs = row_step(rmax, m, C);
+      const PhatScale ps = phat_scale<PH == 2>(PH == 1 ? rmax : bmax, C, rs.mm);
       uint32_t p16[16];
-      const uint4 ph = phat_codes(s, C, rs.neg_big_m, p16);
-      const uint32_t psc = (uint32_t)(int)(rs.e + 127.0f);
+      uint4 ph;
+      if constexpr (PH == 2) ph = phat_codes_direct(s, C, ps.neg_big_m);
+      else ph = phat_codes(s, C, ps.neg_big_m, p16);
+      const uint32_t psc = (uint32_t)(int)(ps.e + 127.0f);
       // ---- normalizer increment: rowsum(P-hat) from the ones column, or the FP32 tree sum
       const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
       v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
       lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
       float lsum = lacc[0];
       if (MODE == 1 || STATS) {
-        const float sb = tree_sum32_h(p16);
-        const float two_e = e8m0_as_float((int)rs.e);
-        if (MODE == 1) lsum = group_sum4(sb) * two_e;
+        // the lane's block sum of FP16 probabilities times its block scale (exact)
+        const float sb = tree_sum32_h(p16) * e8m0_as_float((int)ps.e);
+        if (MODE == 1) lsum = group_sum4(sb);
         if (STATS) {
-          float sp = sb * two_e;
+          float sp = sb;
           sp += __shfl_xor(sp, 16);
           sp += __shfl_xor(sp, 32);
           sp = wave_sum16(sp);
@@ -549,7 +557,7 @@ int gcd_int(int x, int y) {
   return x;
 }
 
-template <int D, bool CAUSAL, int MODE, bool STATS>
+template <int D, bool CAUSAL, int MODE, bool STATS, int PH = 0>
 hipError_t launch4(AttnArgs a, hipStream_t s) {
   constexpr int W = Cfg<D>::kWaves;
   const int group = a.heads_q / a.heads_kv;
@@ -558,14 +566,17 @@ hipError_t launch4(AttnArgs a, hipStream_t s) {
   a.heads_per_wg = hw;
   const int64_t qblocks = (a.len_q + bq - 1) / bq;
   dim3 grid((uint32_t)qblocks, (uint32_t)(a.heads_kv * (group / hw)), (uint32_t)a.batch);
-  hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS>), grid, dim3(Cfg<D>::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS, PH>), grid, dim3(Cfg<D>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch2(const AttnArgs& a, hipStream_t s) {
   const bool stats = a.stats != nullptr;
-  // the round-to-nearest running max (accuracy variant): P-Reordered, no tile statistics
+  // the variants run P-Reordered without tile statistics: the per-tile P-hat scale, Direct-P
+  // codes, the round-to-nearest running max
+  if (a.phat == 1) return launch4<D, CAUSAL, 0, false, 1>(a, s);
+  if (a.phat == 2) return launch4<D, CAUSAL, 0, false, 2>(a, s);
   if (a.max_rule == 1) return launch4<D, CAUSAL, 2, false>(a, s);
   if (a.normalizer == 1) return stats ? launch4<D, CAUSAL, 1, true>(a, s) : launch4<D, CAUSAL, 1, false>(a, s);
   return stats ? launch4<D, CAUSAL, 0, true>(a, s) : launch4<D, CAUSAL, 0, false>(a, s);

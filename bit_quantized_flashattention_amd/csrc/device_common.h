@@ -186,11 +186,33 @@ __device__ __forceinline__ uint32_t quantize_block32(const uint16_t* x, const fl
 // log2(6) rounded to the nearest FP32 (0x40257007): 6 is the largest E2M1 magnitude.
 constexpr float kLog2Six = 0x1.4ae00ep+1f;
 
-// Exponent e of the P-hat scale 2^e of one (query row, key tile), as an integer-valued float:
-// the smallest power of two that keeps the row's largest probability 2^v in the tile inside the
-// E2M1 range, ceil(fp32(v - log2 6)), clamped below at -127 (v = -inf: no visible key).
+// Exponent e of a P-hat scale 2^e (one per query row and 32-key block; per row and tile in the
+// per-tile variant), as an integer-valued float: the smallest power of two that keeps the
+// largest probability 2^v it covers inside the E2M1 range, ceil(fp32(v - log2 6)), clamped below
+// at -127 (v = -inf: no visible key).
 __device__ __forceinline__ float tile_exponent(float v) {
   return fmaxf(__builtin_ceilf(v - kLog2Six), -127.0f);
+}
+
+// Direct-P constants (nearest FP32 values).  delta = 1/4 - log2(1.5)/2: a log2-domain value x is
+// turned into 2^floor(x) (1 + frac(x)), whose E2M1 rounding points (mantissa 1.25 and 1.75) then
+// sit at the log2-domain midpoints of neighbouring E2M1 values once delta is added to the score.
+// kDirectTop = delta - 2.5: that value reaches 6, the largest E2M1 magnitude, at x = 2.5.
+constexpr float kDirectDelta = -0x1.5c01a4p-5f;
+constexpr float kDirectTop = -0x1.457006p+1f;
+
+// Direct-P block exponent: the smallest e keeping the block maximum's value at most 6,
+// ceil(fp32(v + (delta - 2.5))), clamped below at -127.
+__device__ __forceinline__ float direct_exponent(float v) {
+  return fmaxf(__builtin_ceilf(v + kDirectTop), -127.0f);
+}
+
+// float -> uint32 with the hardware conversion's saturation: negative values and -inf give 0
+// (the C cast leaves them undefined, and a clamp would cost a second instruction)
+__device__ __forceinline__ uint32_t cvt_u32_sat(float y) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(y));
+  return r;
 }
 
 // rn16(2^x) of both FP16 halves of h.  v_exp_f16 is correctly rounded on every FP16 input;
@@ -232,9 +254,25 @@ __device__ __forceinline__ float keep_f32(float x) {
 struct RowStep {
   float m_new;      // integer running max ceil(fp32(max S * C)), exact in FP16
   _Float16 alpha;   // rn16(2^(m - m_new)), 0 while m = -inf: the FP16 rescale of O and l
-  float e;          // P-hat scale exponent of the row in this tile (integer-valued)
-  float neg_big_m;  // -(m_new + e): log2-domain offset of the scores relative to 2^e
+  float mm;         // m_new, or a finite stand-in below every real m while m_new = -inf
 };
+
+// The P-hat scale of one lane's 32 keys and the offset of their log2-domain scores, from the
+// largest visible score emax the scale covers (the lane's own block, or the row's tile maximum
+// in the per-tile variant; -inf if none), under code rule DIRECT (Direct-P) or the FP16 exp2.
+struct PhatScale {
+  float e;          // scale exponent (integer-valued); -127 for a block without a visible key
+  float neg_big_m;  // -(mm + e): offset of the scores relative to 2^e
+};
+
+template <bool DIRECT>
+__device__ __forceinline__ PhatScale phat_scale(float emax, float C, float mm) {
+  PhatScale p;
+  const float v = __builtin_fmaf(emax, C, -mm);
+  p.e = DIRECT ? direct_exponent(v) : tile_exponent(v);
+  p.neg_big_m = -(mm + p.e);
+  return p;
+}
 
 // max of two FP32 values that are never NaN, as one v_max_f32 (fmaxf would first quiet operands
 // the compiler cannot prove canonical, such as cross-lane results and loop-carried values)
@@ -254,25 +292,21 @@ __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   r.alpha = __builtin_ldexpf16((_Float16)1.0f, dm);
   // m_new = -inf only for a row with no visible key yet: any finite stand-in below every real
   // m keeps e = -127 and every code 0
-  const float mm = max_nn(r.m_new, -0x1p100f);
-  r.e = tile_exponent(__builtin_fmaf(rmax, C, -mm));
-  r.neg_big_m = -(mm + r.e);
+  r.mm = max_nn(r.m_new, -0x1p100f);
   return r;
 }
 
 // The same step under the round-to-nearest running max (an accuracy variant, not the method's
 // reading): m_new = max(m, rn16(fp32(max S * C))), an FP16 value; alpha = rn16(2^rn16(fp32(m -
 // m_new))) from v_exp_f16 (correctly rounded; 0 while m = -inf, and below 2^-30 where rn16
-// gives 0 anyway); m_new + e is rounded once to FP32.
+// gives 0 anyway); m_new + e is rounded once to FP32 (phat_scale).
 __device__ __forceinline__ RowStep row_step_nearest16(float rmax, float m, float C) {
   RowStep r;
   r.m_new = max_nn(m, (float)(_Float16)(rmax * C));
   const float d = m - r.m_new;
   const uint32_t a2 = exp2_h2(pack_h2(d, d));
   r.alpha = d >= -30.0f ? __builtin_bit_cast(h2, a2)[0] : (_Float16)0.0f;
-  const float mm = max_nn(r.m_new, -0x1p100f);
-  r.e = tile_exponent(__builtin_fmaf(rmax, C, -mm));
-  r.neg_big_m = -(mm + r.e);
+  r.mm = max_nn(r.m_new, -0x1p100f);
   return r;
 }
 
@@ -317,6 +351,41 @@ __device__ __forceinline__ uint4 phat_codes(const float* s, float C, float nbm, 
       if (j == 3) x = cvt_fp4x2_h<3>(x, pr);
     }
     w[q] = x;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Direct-P codes of a lane's 32 keys (FA4 prior art: scores mapped straight to FP4
+// probabilities, no exponential): with K = fp32(fp32(127 - (m + e)) + delta), the single FP32
+// rounding y = fma(s_k, C 2^23, K 2^23) holds (x + 127) 2^23 for the log2-domain value
+// x = fma32(s_k, C, K) - 127; its integer part (0 for y <= 0, so a masked key gives 0), read as
+// the bits of an FP32 number, is 2^floor(x) (1 + frac(x)), and the converter rounds that to E2M1
+// (RNE, saturating at 6).  Packed two per byte in key order like phat_codes.
+__device__ __forceinline__ uint4 phat_codes_direct(float* s, float C, float neg_big_m) {
+  const float k = (127.0f + neg_big_m) + kDirectDelta;
+  const float b = k * 0x1p23f;
+  const float c23 = C * 0x1p23f;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    // the values replace the scores in place, eight keys at a time (no second set of live registers)
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int i = s_index(8 * q + j);
+      s[i] = __uint_as_float(cvt_u32_sat(__builtin_fmaf(s[i], c23, b)));
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int kk = 8 * q + 2 * j;
+      const float z0 = s[s_index(kk)], z1 = s[s_index(kk + 1)];
+      if (j == 0) x = cvt_fp4x2<0>(x, z0, z1, 1.0f);
+      if (j == 1) x = cvt_fp4x2<1>(x, z0, z1, 1.0f);
+      if (j == 2) x = cvt_fp4x2<2>(x, z0, z1, 1.0f);
+      if (j == 3) x = cvt_fp4x2<3>(x, z0, z1, 1.0f);
+    }
+    w[q] = x;
+    __builtin_amdgcn_sched_barrier(0);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }

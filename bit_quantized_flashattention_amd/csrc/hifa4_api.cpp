@@ -95,6 +95,15 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
   if (o->kv_tile != 64 && o->kv_tile != 128) return fail(HIFA4_ERR_UNSUPPORTED, "kv_tile must be 64 or 128");
   if (o->max_rule != HIFA4_MAX_CEIL && o->max_rule != HIFA4_MAX_NEAREST16)
     return fail(HIFA4_ERR_SHAPE, "max_rule must be HIFA4_MAX_CEIL or HIFA4_MAX_NEAREST16");
+  if (o->phat_scale != HIFA4_PHAT_BLOCK32 && o->phat_scale != HIFA4_PHAT_TILE)
+    return fail(HIFA4_ERR_SHAPE, "phat_scale must be HIFA4_PHAT_BLOCK32 or HIFA4_PHAT_TILE");
+  if (o->phat_rule != HIFA4_PHAT_EXP16 && o->phat_rule != HIFA4_PHAT_DIRECT)
+    return fail(HIFA4_ERR_SHAPE, "phat_rule must be HIFA4_PHAT_EXP16 or HIFA4_PHAT_DIRECT");
+  if (o->phat_rule == HIFA4_PHAT_DIRECT && o->phat_scale != HIFA4_PHAT_BLOCK32)
+    return fail(HIFA4_ERR_UNSUPPORTED, "HIFA4_PHAT_DIRECT takes one scale per 32-key block (HIFA4_PHAT_BLOCK32)");
+  if ((o->phat_rule != HIFA4_PHAT_EXP16 || o->phat_scale != HIFA4_PHAT_BLOCK32) &&
+      (o->normalizer != HIFA4_P_REORDERED || o->max_rule != HIFA4_MAX_CEIL))
+    return fail(HIFA4_ERR_UNSUPPORTED, "the P-hat variants run P-Reordered with HIFA4_MAX_CEIL");
   if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
   if (o->kv_capacity != 0 &&
@@ -351,6 +360,7 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
   a.causal = opts->causal;
   a.normalizer = opts->normalizer;
   a.max_rule = opts->max_rule;
+  a.phat = opts->phat_rule == HIFA4_PHAT_DIRECT ? 2 : (opts->phat_scale == HIFA4_PHAT_TILE ? 1 : 0);
   a.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
   hipStream_t stream = (hipStream_t)hip_stream;
   hipError_t e;
@@ -360,6 +370,8 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
     if (a.stats || a.normalizer != HIFA4_P_REORDERED)
       return fail(HIFA4_ERR_UNSUPPORTED, "attention: HIFA4_MAX_NEAREST16 runs P-Reordered without tile statistics");
   }
+  if (a.stats && a.phat != 0)
+    return fail(HIFA4_ERR_UNSUPPORTED, "attention: the P-hat variants run without tile statistics");
   if (dims->len_q == 1) {
     if (a.stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
     const size_t need = hifa4_attention_workspace_bytes(dims, opts);

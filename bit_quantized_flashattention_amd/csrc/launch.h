@@ -55,6 +55,8 @@ struct AttnArgs {
   int32_t causal;
   int32_t normalizer;
   int32_t max_rule;     // 0: integer running max (the method's reading); 1: round-to-nearest FP16 (prefill)
+  int32_t phat;         // P-hat rule: 0 per (row, 32-key block) from FP16 probabilities (the method's
+                        // reading); 1 per (row, tile) (variant); 2 Direct-P codes per 32-key block
   int32_t num_splits;
   int32_t tiles_per_split;
   int32_t heads_per_wg;  // prefill: query heads served by one work-group (set by the launcher)

@@ -77,6 +77,21 @@ enum { HIFA4_P_REORDERED = 0, HIFA4_INCONSISTENT = 1 };
    tile statistics. */
 enum { HIFA4_MAX_CEIL = 0, HIFA4_MAX_NEAREST16 = 1 };
 
+/* P-hat scale granularity.  HIFA4_PHAT_BLOCK32 is the method as this library reads the HiFA4
+   abstract (P-hat is the 4-bit operand of the PV product, so it takes the 4-bit block format):
+   one power-of-two scale per (query row, 32-key block).  HIFA4_PHAT_TILE is an accuracy variant
+   with one scale per (query row, key tile), from the row's largest score in the tile. */
+enum { HIFA4_PHAT_BLOCK32 = 0, HIFA4_PHAT_TILE = 1 };
+
+/* P-hat code rule.  HIFA4_PHAT_EXP16 (the method): the E2M1 codes of the FP16 probabilities
+   rn16(2^rn16(u)).  HIFA4_PHAT_DIRECT (Direct-P, after the "Hardware-Aware FP4 FlashAttention-4"
+   abstract, which maps scores straight to FP4 probabilities): no exponential; the log2-domain score
+   x = fma32(S, C, K), K = fp32(fp32(127 - (m + e)) + delta) - 127 with delta = fp32(1/4 -
+   log2(1.5)/2), becomes 2^floor(x) (1 + frac(x)) (mantissa truncated to 23 bits), rounded to E2M1;
+   the block exponent is e = max(-127, ceil(fp32(fma32(max S, C, -m) + fp32(delta - 2.5)))).
+   Codes of value >= 1 then go to the E2M1 value nearest in the log2 domain. */
+enum { HIFA4_PHAT_EXP16 = 0, HIFA4_PHAT_DIRECT = 1 };
+
 typedef struct {
   int32_t causal;     /* 0 or 1 */
   int32_t normalizer; /* HIFA4_P_REORDERED: l from P-hat (the method); HIFA4_INCONSISTENT: l from
@@ -91,11 +106,14 @@ typedef struct {
                           hold with Lk (Lk32) replaced by kv_capacity (rounded up to 32) for the
                           strides, while Lk keys are attended */
   int32_t max_rule;    /* HIFA4_MAX_CEIL (0) or HIFA4_MAX_NEAREST16 (1, prefill only) */
+  int32_t phat_scale;  /* HIFA4_PHAT_BLOCK32 (0, the method) or HIFA4_PHAT_TILE (1) */
+  int32_t phat_rule;   /* HIFA4_PHAT_EXP16 (0, the method) or HIFA4_PHAT_DIRECT (1, with
+                          HIFA4_PHAT_BLOCK32 only) */
 } hifa4_attn_opts;
 
 /*
- * Smooth-QK calibration (host, synchronous).  [HiFA4 Abstract: the scale factors are computed
- * once from a small offline calibration set.]  q_cal FP16 bits [Hq, N, d], k_cal FP16 bits
+ * Smooth-QK calibration (host, synchronous).  [HiFA4 Abstract: the per-channel Smooth-QK factors
+ * are static, derived once offline from calibration data.]  q_cal FP16 bits [Hq, N, d], k_cal FP16 bits
  * [Hkv, N, d] (post-RoPE).  Per (KV head g, channel j): aK = max|k_cal[g, :, j]|, aQ = max over
  * the tokens and the query heads of group g of |q_cal|.  Gate: rho = max(aK) / median(aK) over
  * all (g, j); Smooth-QK is on iff rho >= gate_tau.  s = aK^alpha / aQ^(1-alpha) where on and both
@@ -191,10 +209,12 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * online-softmax state in FP16, P-Reordering fused into the PV product.]
  * Per query row and per tile of kv_tile keys (ascending): S = Q-hat K-hat^T on the scaled FP4
  * matrix cores; m_new = max(m, ceil(fp32(max S * C))) with C = fp32(log2(e)/sqrt(d));
- * P-hat = E2M1 codes with one power-of-two scale 2^e per (query row, tile) ("each probability
- * tile is quantized"), e = ceil(fp32(v - log2 6)) with v = fma(max S, C, -m_new), of the FP16
- * probabilities rn16(2^rn16(fma(S, C, -(m_new + e)))) (P-tilde = 2^e times those); PV and the
- * l-increment = rowsum(P-hat) from the same matrix-core pass; the state update is FP16
+ * P-hat = E2M1 codes with one power-of-two scale 2^e per (query row, 32-key block) (P-hat is the
+ * 4-bit operand of the PV product, so it takes the 4-bit block format), e = ceil(fp32(v - log2 6))
+ * with v = fma(max over the block's visible S, C, -m_new) (-127 for a block without a visible
+ * key), of the FP16 probabilities rn16(2^rn16(fma(S, C, -(m_new + e)))) (P-tilde = 2^e times
+ * those); opts->phat_scale and opts->phat_rule select the variants above.  PV and the
+ * l-increment = rowsum(P-hat) come from the same matrix-core pass; the state update is FP16
  * arithmetic, O = fma16(rn16(2^(m_old - m_new)), O, rn16(PV)), l likewise; out = fp16(O / l).
  * Lq == 1 runs split-KV decode (num_splits partial FP16 states in the workspace, merged in
  * split order); Lq > 1 runs the prefill kernel (workspace unused, may be NULL).
@@ -203,6 +223,8 @@ size_t hifa4_attention_workspace_bytes(const hifa4_dims* dims, const hifa4_attn_
  * a row block never visits); prefill only.
  * Under opts->max_rule = HIFA4_MAX_NEAREST16 the running max and the rescale follow that rule
  * (see the enum); Lq == 1, INCONSISTENT or tile_stats then return HIFA4_ERR_UNSUPPORTED.
+ * HIFA4_PHAT_TILE and HIFA4_PHAT_DIRECT run P_REORDERED with HIFA4_MAX_CEIL and without
+ * tile_stats (HIFA4_ERR_UNSUPPORTED otherwise; HIFA4_PHAT_DIRECT with HIFA4_PHAT_TILE too).
  * Errors: HIFA4_ERR_NULL, HIFA4_ERR_SHAPE, HIFA4_ERR_UNSUPPORTED, HIFA4_ERR_WORKSPACE,
  * HIFA4_ERR_ALIGNMENT, HIFA4_ERR_HIP.
  */

@@ -46,7 +46,7 @@ def compare_out(got, want, label=""):
 
 
 def run_case(q, k, v, causal, kv_tile, normalizer=A.P_REORDERED, alpha=0.5, calib=None, num_splits=0,
-             stats=False, smooth_on=True, max_rule=A.MAX_CEIL):
+             stats=False, smooth_on=True, max_rule=A.MAX_CEIL, phat_scale=A.PHAT_BLOCK32, phat_rule=A.PHAT_EXP16):
     """Product path (library calibrate + GPU quantize + GPU attention) and the oracle on the same inputs."""
     import torch
     b, hq, lq, d = q.shape
@@ -64,12 +64,13 @@ def run_case(q, k, v, causal, kv_tile, normalizer=A.P_REORDERED, alpha=0.5, cali
     dims = hf.make_dims(b, hq, hkv, d, lq, lk)
     splits_used = hf.decode_num_splits(dims, hf.make_opts(causal, normalizer, kv_tile, num_splits))
     r = hf.attention_fwd(res, dims, causal, normalizer, kv_tile, num_splits, tile_stats=True if stats else None,
-                         max_rule=max_rule)
+                         max_rule=max_rule, phat_scale=phat_scale, phat_rule=phat_rule)
     out, st = (r if stats else (r, None))
     # the fused-Q entry point must reproduce the two-call path bit for bit
     kv_only = {n: res[n] for n in NAMES[2:]}
     r16 = hf.attention_fwd(kv_only, dims, causal, normalizer, kv_tile, num_splits, tile_stats=True if stats else None,
-                           q16=(to_dev(q), to_dev(s) if s is not None else None), max_rule=max_rule)
+                           q16=(to_dev(q), to_dev(s) if s is not None else None), max_rule=max_rule,
+                           phat_scale=phat_scale, phat_rule=phat_rule)
     out16, st16 = (r16 if stats else (r16, None))
     torch.cuda.synchronize()
     assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q output differs"
@@ -77,5 +78,8 @@ def run_case(q, k, v, causal, kv_tile, normalizer=A.P_REORDERED, alpha=0.5, cali
         assert torch.equal(st16, st), "fused-Q tile statistics differ"
     diag = A.Diag()
     want = A.attention_p(qq, causal, kv_tile, normalizer, num_splits=splits_used if lq == 1 else 1, diag=diag,
-                         max_rule=max_rule)
+                         max_rule=max_rule, phat_scale=phat_scale, phat_rule=phat_rule)
+    # sums the matrix instructions cannot return exactly: there the accumulation model decides
+    print("  inexact sums (oracle): scores %d/%d, PV %d/%d, l %d"
+          % (diag.inexact_s, diag.total_s, diag.inexact_pv, diag.total_pv, diag.inexact_l))
     return out.cpu().numpy(), want, qq, diag, (st.cpu().numpy() if st is not None else None)

@@ -101,8 +101,10 @@ def test_attention_rejects_bad_arguments_without_launching(L):
 
 
 def test_max_rule_is_validated_and_limited_to_prefill(L):
-    # hifa4_attn_opts: four int32, the int64 capacity at offset 16, max_rule at 24, padded to 32
-    assert ctypes.sizeof(hf.Opts) == 32 and hf.Opts.max_rule.offset == 24
+    # hifa4_attn_opts: four int32, the int64 capacity at offset 16, max_rule at 24, phat_scale at
+    # 28, phat_rule at 32, padded to 40
+    assert ctypes.sizeof(hf.Opts) == 40 and hf.Opts.max_rule.offset == 24
+    assert hf.Opts.phat_scale.offset == 28 and hf.Opts.phat_rule.offset == 32
     dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     pre = hf.make_dims(1, 4, 2, 128, 64, 64)
     st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(hf.make_opts(max_rule=2)), *([dummy] * 7), None, 0, None, None)
@@ -117,6 +119,24 @@ def test_max_rule_is_validated_and_limited_to_prefill(L):
     stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
     st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(near), *([dummy] * 7), None, 0, stats, None)
     assert st == 3 and b"statistics" in L.hifa4_last_error()
+
+
+def test_phat_options_are_validated(L):
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    pre = hf.make_dims(1, 4, 2, 128, 64, 64)
+
+    def call(o, stats=None):
+        return L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(o), *([dummy] * 7), None, 0, stats, None)
+    assert call(hf.make_opts(phat_scale=2)) == 2 and b"phat_scale" in L.hifa4_last_error()
+    assert call(hf.make_opts(phat_rule=5)) == 2 and b"phat_rule" in L.hifa4_last_error()
+    # Direct-P takes per-block scales; the variants run P-Reordered with the integer running max
+    assert call(hf.make_opts(phat_scale=hf.PHAT_TILE, phat_rule=hf.PHAT_DIRECT)) == 3
+    for o in [hf.make_opts(normalizer=hf.INCONSISTENT, phat_rule=hf.PHAT_DIRECT),
+              hf.make_opts(normalizer=hf.INCONSISTENT, phat_scale=hf.PHAT_TILE),
+              hf.make_opts(max_rule=hf.MAX_NEAREST16, phat_rule=hf.PHAT_DIRECT)]:
+        assert call(o) == 3 and b"P-Reordered" in L.hifa4_last_error()
+    stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
+    assert call(hf.make_opts(phat_rule=hf.PHAT_DIRECT), stats) == 3 and b"statistics" in L.hifa4_last_error()
 
 
 def test_size_limits_are_rejected(L):

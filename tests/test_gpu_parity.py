@@ -215,3 +215,27 @@ def test_round_to_nearest_running_max(cfg_id, b, hq, hkv, lq, lk, d, causal, kv_
     # the variant is a different function of the same codes: it must differ from the method's output
     _, want_ceil, *_ = run_case(q, k, v, causal, kv_tile, calib=cal, alpha=cfg["alpha"])
     assert np.count_nonzero(want_ceil.view(np.uint16) != want.view(np.uint16)) > 0
+
+
+@pytest.mark.parametrize("cfg_id,b,hq,hkv,lq,lk,d,causal,kv_tile", [
+    (0, 1, 2, 2, 128, 128, 64, False, 64),     # the tiny non-causal workload
+    (1, 1, 8, 2, 300, 300, 128, True, 128),    # Qwen-shaped, reduced
+    (1, 3, 6, 3, 17, 129, 128, True, 64),      # ragged: a key past a tile, rows past a 16-row block
+    (1, 1, 4, 1, 77, 333, 128, True, 128),     # causal with Lq < Lk
+    (1, 2, 2, 2, 100, 300, 128, False, 128),   # non-causal, ragged key tail
+    (3, 1, 4, 2, 200, 200, 256, True, 128),    # Gemma-shaped d = 256
+    (1, 3, 8, 2, 1, 1000, 128, True, 128),     # decode (split-KV)
+    (3, 2, 4, 2, 1, 700, 256, True, 64),       # decode, d = 256, 64-key tiles
+])
+@pytest.mark.parametrize("variant", ["tile", "direct"])
+def test_phat_variants(cfg_id, b, hq, hkv, lq, lk, d, causal, kv_tile, variant):
+    """P-hat variants against the oracle's: one scale per (row, tile) (HIFA4_PHAT_TILE), and
+    Direct-P codes built straight from the log2-domain score (HIFA4_PHAT_DIRECT); both entry
+    points, prefill and split-KV decode.  Each must also differ from the method's output."""
+    cfg, q, k, v, cal = gen(cfg_id, B=b, Hq=hq, Hkv=hkv, Lq=lq, Lk=lk, d=d)
+    kw = dict(phat_scale=A.PHAT_TILE) if variant == "tile" else dict(phat_rule=A.PHAT_DIRECT)
+    print("case phat", variant, cfg_id, b, hq, hkv, lq, lk, d, causal, kv_tile, flush=True)
+    got, want, *_ = run_case(q, k, v, causal, kv_tile, calib=cal, alpha=cfg["alpha"], **kw)
+    compare_out(got, want, "phat-%s-%d-%d-%d" % (variant, lq, lk, d))
+    _, want_method, *_ = run_case(q, k, v, causal, kv_tile, calib=cal, alpha=cfg["alpha"])
+    assert np.count_nonzero(want_method.view(np.uint16) != want.view(np.uint16)) > 0
