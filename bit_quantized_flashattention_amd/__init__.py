@@ -70,6 +70,9 @@ def lib():
             [ctypes.c_int64] + [_vp] * 6 + \
             [ctypes.c_size_t, _vp, _vp]
         L.hifa4_attention_fwd_q16.restype = ctypes.c_int
+        L.hifa4_attention_fwd_q16_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts)] + [_vp] * 4 + \
+            [ctypes.c_int64] + [_vp] * 7
+        L.hifa4_attention_fwd_q16_noalloc.restype = ctypes.c_int
         L.hifa4_status_string.argtypes = [ctypes.c_int]
         L.hifa4_status_string.restype = ctypes.c_char_p
         L.hifa4_last_error.argtypes = []
@@ -308,3 +311,25 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
             _ptr(qkv["k_scales"]), _ptr(qkv["v_codes"]), _ptr(qkv["v_scales"]), _ptr(out), _ptr(workspace),
             workspace.numel() if workspace is not None else 0, _ptr(stats), _stream(stream)))
     return (out, stats) if tile_stats is not None else out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # the library's fixed decode scratch per GPU (hifa4.h)
+
+
+def attention_fwd_q16_noalloc(kv, q, s, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
+                              out=None, stream=None, rope_cos=None, rope_sin=None, kv_capacity=0, max_rule=MAX_CEIL,
+                              phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
+    """hifa4_attention_fwd_q16_noalloc: the fused-Q forward with decode partials in the library's fixed
+    device scratch (no workspace).  kv: dict with the K-hat / V-hat tensors; q FP16 [B, Hq, Lq, d];
+    s the Smooth-QK scales or None.  ``out`` must be given by callers that cannot allocate."""
+    import torch
+    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule, phat_scale, phat_rule)
+    if out is None:
+        out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16,
+                          device=kv["k_codes"].device)
+    n_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    _check(lib().hifa4_attention_fwd_q16_noalloc(
+        ctypes.byref(dims), ctypes.byref(opts), _ptr(q), _ptr(s), _ptr(rope_cos), _ptr(rope_sin), n_pos,
+        _ptr(kv["k_codes"]), _ptr(kv["k_scales"]), _ptr(kv["v_codes"]), _ptr(kv["v_scales"]), _ptr(out), None,
+        _stream(stream)))
+    return out

@@ -5,6 +5,8 @@
 // tile ahead of the computation.  The query heads of a GQA group are the MFMA columns (the
 // same S^T = K-hat Q-hat^T layout as the prefill kernel, see attn_prefill.hip), so a wave
 // serves one (batch, KV head, split) and keeps its split's FP16 state in registers.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -273,6 +275,38 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
     case 256: return launch_d<256>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ---- fixed device scratch for callers that cannot allocate (hifa4_attention_fwd_q16_noalloc)
+//
+// The split partials of one decode call live in this array instead of a caller workspace.  Each
+// GPU the library runs on holds its own copy (at its own address) until the process ends.  In
+// host code the name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of scratch per device, nullptr until looked up
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace hifa4

@@ -455,4 +455,27 @@ hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_op
   return attention_launch(a, dims, opts, workspace, workspace_bytes, hip_stream);
 }
 
+hifa4_status hifa4_attention_fwd_q16_noalloc(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
+                                             const float* s, const float* rope_cos, const float* rope_sin,
+                                             int64_t rope_positions, const void* k_codes, const void* k_scales,
+                                             const void* v_codes, const void* v_scales, void* out,
+                                             float* tile_stats, void* hip_stream) {
+  hifa4_status st = check_dims(dims);
+  if (st != HIFA4_OK) return st;
+  st = check_opts(dims, opts);
+  if (st != HIFA4_OK) return st;
+  const size_t need = hifa4_attention_workspace_bytes(dims, opts);
+  if (need > hifa4::kDecodeScratchBytes)
+    return fail(HIFA4_ERR_WORKSPACE, "attention (no-alloc): decode partials need " + std::to_string(need) +
+                                         " bytes, beyond the fixed scratch of " +
+                                         std::to_string(hifa4::kDecodeScratchBytes) + " bytes");
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = hifa4::decode_scratch(&ws);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("attention (no-alloc): scratch lookup: ") + hipGetErrorString(e));
+  }
+  return hifa4_attention_fwd_q16(dims, opts, q, s, rope_cos, rope_sin, rope_positions, k_codes, k_scales, v_codes,
+                                 v_scales, out, ws, need, tile_stats, hip_stream);
+}
+
 }  // extern "C"

@@ -106,4 +106,9 @@ hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 
+// Bytes of the library's fixed decode scratch (one array per device, see decode_scratch).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+// Device address of the current device's decode scratch (looked up once per device).
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace hifa4

@@ -254,6 +254,26 @@ hifa4_status hifa4_attention_fwd_q16(const hifa4_dims* dims, const hifa4_attn_op
                                      const void* v_codes, const void* v_scales, void* out, void* workspace,
                                      size_t workspace_bytes, float* tile_stats, void* hip_stream);
 
+/*
+ * hifa4_attention_fwd_q16 without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Decode (Lq == 1) keeps its split partials in a fixed device array of the library, 8 MiB
+ * (8388608 bytes) per GPU, held from the first call on that GPU until the process ends; prefill
+ * needs no scratch.  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device looks up the array's device address once.  Every other
+ * argument, the output and the errors are those of hifa4_attention_fwd_q16, plus
+ * HIFA4_ERR_WORKSPACE when hifa4_attention_workspace_bytes(dims, opts) exceeds 8 MiB.  The
+ * partials are fully rewritten by every decode call before they are read, so nothing needs
+ * clearing between calls; but all calls on one GPU share the one array, so calls that may
+ * overlap on one GPU (on different streams, or from several threads) race and must be ordered
+ * by the caller.
+ */
+hifa4_status hifa4_attention_fwd_q16_noalloc(const hifa4_dims* dims, const hifa4_attn_opts* opts, const void* q,
+                                             const float* s, const float* rope_cos, const float* rope_sin,
+                                             int64_t rope_positions, const void* k_codes, const void* k_scales,
+                                             const void* v_codes, const void* v_scales, void* out,
+                                             float* tile_stats, void* hip_stream);
+
 /* Static description of a status code. */
 const char* hifa4_status_string(hifa4_status status);
 

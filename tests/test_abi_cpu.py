@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -137,6 +137,17 @@ def test_phat_options_are_validated(L):
         assert call(o) == 3 and b"P-Reordered" in L.hifa4_last_error()
     stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
     assert call(hf.make_opts(phat_rule=hf.PHAT_DIRECT), stats) == 3 and b"statistics" in L.hifa4_last_error()
+
+
+def test_noalloc_rejects_partials_beyond_the_fixed_scratch(L):
+    dummy = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    big = hf.make_dims(256, 64, 8, 256, 1, 1 << 16)
+    o = hf.make_opts(causal=True, num_splits=4)
+    need = hf.attention_workspace_bytes(big, o)
+    assert need > hf.NOALLOC_SCRATCH_BYTES
+    st = L.hifa4_attention_fwd_q16_noalloc(ctypes.byref(big), ctypes.byref(o), dummy, None, None, None, 0,
+                                           *([dummy] * 5), None, None)
+    assert st == 4 and b"scratch" in L.hifa4_last_error()
 
 
 def test_size_limits_are_rejected(L):
