@@ -1,30 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the 4-bit (HiFA4-style) attention forward on one MI355X.
 
-A step is one pass of the hot path over one batch of resident synthetic input:
-the Smooth-QK rescale + 4-bit quantization of K and V (HBM-bound kernels) followed
-by the fused 4-bit attention forward, which rescales and quantizes its own query
-rows on the way in (hifa4_attention_fwd_q16).  The default workload is the batched
-causal prefill (B=8, L=4096, Hq=32/Hkv=8, d=128, P-Reordered normalizer, 128-key
-tiles).  The JSON line also carries the memory-bound split-KV decode (B=64,
-Lk=32768, pre-quantized cache; a step runs split, with the query token quantized
-in-kernel, and merge).  The default warm-up (50 steps, about 40 ms) lets the GPU
-clocks settle before the timed steps.  The line also carries the same prefill step from
-pre-RoPE Q and K (rope_prefill: K/V quantized with RoPE by hifa4_quantize_qkv_rope, the query
-quantized in the RoPE quantizer too, then the attention from the codes).
+A step is one pass of the hot path over one batch of resident synthetic input: the Smooth-QK
+rescale + 4-bit quantization of K and V (HBM-bound kernels) followed by the fused 4-bit attention
+forward, which rescales and quantizes its own query rows on the way in
+(hifa4_attention_fwd_q16).  The headline workload is the batched causal prefill (B=8, L=4096,
+Hq=32/Hkv=8, d=128, P-Reordered normalizer, P-hat with one scale per 32-key block, 128-key
+tiles).  The JSON line also carries, each with its own roofline:
+  prefill_d256       the Gemma2-9B-shaped causal prefill (B=2, L=8192, Hq=16/Hkv=8, d=256);
+  direct_p           the headline workload with Direct-P codes (no exponential per score);
+  noncausal          the headline shapes without the causal mask, with the method's codes and
+                     with Direct-P codes (the Direct-P page's setting is non-causal inference);
+  rope_prefill       the headline step from pre-RoPE Q and K (RoPE fused into the quantizer);
+  decode             the memory-bound split-KV decode (B=64, Lk=32768, pre-quantized cache),
+                     with the cache append of one key per sequence;
+  cpu_baseline       the oracle timed on the host's cores on a bounded sample, run last.
 
-    python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline] [--legs a,b,...]
 
-Rates: algorithmic FLOPs are 4 * d per visible (query, key) pair (L(L+1)/2 pairs
-per head when causal); decode bytes are the K-hat/V-hat codes and scales, the FP16
-query, the Smooth-QK scales and the FP16 output.  Kernel durations come from HIP events recorded on the
-stream the kernels run on.  Peaks: MI355X dense FP4 MFMA 10.1 PFLOP/s, HBM3E
-8 TB/s (AMD's published figures).
+Every leg runs W untimed warm-up steps and keeps warming up for at least 0.3 s (the GPU clocks
+settle), then times exactly K steps between two device synchronizations.  Kernel durations come
+from HIP events recorded on the stream the kernels run on; the line gives their mean and, per
+leg, median, min and max.  Rates: algorithmic FLOPs are 4 * d per visible (query, key) pair
+(L(L+1)/2 pairs per head when causal); decode bytes are the K-hat/V-hat codes and scales, the
+FP16 query, the Smooth-QK scales and the FP16 output.  Peaks: MI355X dense FP4 MFMA
+10.1 PFLOP/s, HBM3E 8 TB/s (AMD's published figures).
 """
 import argparse
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -33,29 +38,38 @@ sys.path.insert(0, ROOT)
 
 FP4_PEAK_TFLOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
+MIN_WARM_S = 0.3
 COPY_PROBE_BYTES = 512 << 20  # plain device copy run by --traffic-probe to calibrate the counters
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["attn_prefill.hip", "attn_decode.hip", "device_common.h", "quantize.hip"]
+ALL_LEGS = ["prefill_d256", "direct_p", "noncausal", "rope_prefill", "decode"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--legs", default=",".join(ALL_LEGS), help="comma-separated extra legs (%s)" % ",".join(ALL_LEGS))
     p.add_argument("--no-decode", action="store_true")
-    p.add_argument("--no-rope", action="store_true", help="skip the pre-RoPE (fused RoPE prologue) variant of the step")
+    p.add_argument("--no-rope", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing sample")
-    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill-d256", "prefill-L2048"])
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="per-worker budget of the oracle sample")
     p.add_argument("--traffic-probe", action="store_true",
                    help="also run one plain %d MiB device copy (counter calibration for HBM traffic)"
                         % (COPY_PROBE_BYTES >> 20))
-    return p.parse_args()
+    a = p.parse_args()
+    legs = [x for x in a.legs.split(",") if x]
+    if a.no_decode and "decode" in legs:
+        legs.remove("decode")
+    if a.no_rope and "rope_prefill" in legs:
+        legs.remove("rope_prefill")
+    a.leg_list = legs
+    return a
 
 
 def kernel_source_digest():
-    """sha256 over the kernel sources: the HBM-traffic figures are valid only for these bytes."""
+    """sha256 over the kernel sources: counter figures are valid only for these bytes."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -64,26 +78,32 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def traffic_for(key):
-    """HBM bytes per launch of a kernel from the committed counter summary, or None.
+def counters_for(key):
+    """Counter figures of one kernel from the committed summary, or None.
 
-    profiles/traffic.json holds FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of each kernel and
-    of a plain copy of known size measured in the same runs; each counter is scaled by
-    bytes_copied / counter(copy).  The figures are dropped when the kernel sources changed
-    since they were taken.
+    profiles/counters.json holds, per kernel and workload, FETCH_SIZE / WRITE_SIZE per dispatch
+    (KiB; scaled by bytes_copied / counter(copy) of a plain copy of known size measured in the
+    same runs) and the matrix-core / vector-ALU busy fractions of its issue-counter run.  The
+    figures are dropped when the kernel sources changed since they were taken.
     """
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_digest() or key not in t.get("kernels", {}):
         return None
     k = t["kernels"][key]
-    cp = t["copy"]
-    f_scale = cp["bytes"] / (cp["fetch_kib"] * 1024.0)
-    w_scale = cp["bytes"] / (cp["write_kib"] * 1024.0)
-    return int(round(k["fetch_kib"] * 1024.0 * f_scale + k["write_kib"] * 1024.0 * w_scale))
+    out = {}
+    cp = t.get("copy")
+    if cp and "fetch_kib" in k and "write_kib" in k:
+        f_scale = cp["bytes"] / (cp["fetch_kib"] * 1024.0)
+        w_scale = cp["bytes"] / (cp["write_kib"] * 1024.0)
+        out["traffic"] = int(round(k["fetch_kib"] * 1024.0 * f_scale + k["write_kib"] * 1024.0 * w_scale))
+    for name in ("mfma_busy", "valu_busy"):
+        if name in k:
+            out[name] = k[name]
+    return out
 
 
 def copy_probe():
@@ -102,12 +122,56 @@ def causal_pairs(lq, lk):
     return sum(min(lk, r + shift + 1) for r in range(lq))
 
 
-def bench_prefill(args, cfg_id):
+def timed(step, n_events, args):
+    """Warm up (args.warmup steps and at least MIN_WARM_S seconds), then time args.steps steps.
+
+    step(ev) runs one step; ev is None or a list of n_events HIP events it records on its stream.
+    Returns (wall ms per step, list per timed step of the n_events - 1 event intervals in ms)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < MIN_WARM_S:
+        step(None)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(args.steps)]
+    t1 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    gaps = [[e[j].elapsed_time(e[j + 1]) for j in range(n_events - 1)] for e in evs]
+    return (t2 - t1) * 1e3 / args.steps, gaps
+
+
+def spread(ms):
+    """Mean, median, min and max of per-step times (ms)."""
+    return {"mean": round(statistics.fmean(ms), 4), "median": round(statistics.median(ms), 4),
+            "min": round(min(ms), 4), "max": round(max(ms), 4)}
+
+
+def mfma_roofline(flops, kernel_ms, counters):
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+         "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 4)}
+    if counters:
+        r["traffic"] = counters.get("traffic")
+        if "mfma_busy" in counters:
+            r["mfma_busy"] = counters["mfma_busy"]
+            r["valu_busy"] = counters.get("valu_busy")
+    return r
+
+
+def bench_prefill(args, cfg_id, causal=None, phat_rule=0, counter_key=None):
+    """One prefill leg: per step, K/V quantize, then the attention with Q quantized in-kernel."""
     import torch
     import bit_quantized_flashattention_amd as hf
     import synth
 
     cfg = synth.config(cfg_id)
+    causal = cfg["causal"] if causal is None else causal
     b, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
     q, k, v = synth.make_qkv_device(cfg)
     q_cal, k_cal = synth.make_calibration(cfg)
@@ -115,38 +179,40 @@ def bench_prefill(args, cfg_id):
     sd = torch.from_numpy(s).cuda()
     invd = torch.from_numpy(inv).cuda()
     dims = hf.make_dims(b, hq, hkv, d, lq, lk)
-    qkv = hf.quantize_qkv(q, k, v, sd, invd, dims=dims)
+    qkv = hf.quantize_qkv(None, k, v, sd, invd, dims=dims)
     out = torch.empty((b, hq, lq, d), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev):
         # K-hat, V-hat from the quantizer; Q is rescaled and quantized inside the attention kernel
         hf.quantize_qkv(None, k, v, sd, invd, dims=dims, out=qkv)
         if ev is not None:
             ev[0].record(stream)
-        hf.attention_fwd(qkv, dims, cfg["causal"], hf.P_REORDERED, cfg["kv_tile"], out=out, q16=(q, sd))
+        hf.attention_fwd(qkv, dims, causal, hf.P_REORDERED, cfg["kv_tile"], out=out, q16=(q, sd), phat_rule=phat_rule)
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    attn_ms = sum(a.elapsed_time(c) for a, c in evs) / args.steps
-    step_ms = (t1 - t0) * 1e3 / args.steps
-    pairs = causal_pairs(lq, lk) if cfg["causal"] else lq * lk
+    step_ms, gaps = timed(step, 2, args)
+    attn = [g[0] for g in gaps]
+    attn_ms = statistics.fmean(attn)
+    pairs = causal_pairs(lq, lk) if causal else lq * lk
     flops = 4.0 * d * pairs * b * hq
-    return dict(cfg=cfg, step_ms=step_ms, attn_ms=attn_ms, flops=flops, gate=gate,
-                qkv_inputs=(q, k, v), qkv=qkv, out=out)
+    res = {
+        "workload": "%s: %s B%d Hq%d/Hkv%d d%d L%d, kv_tile %d, P-hat %s; per step: K/V quantize + attention with Q quantized in-kernel"
+                    % (cfg["name"], "causal" if causal else "non-causal", b, hq, hkv, d, lq, cfg["kv_tile"],
+                       "Direct-P codes" if phat_rule else "exp16 codes, one scale per 32-key block"),
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
+        "attention_ms": spread(attn),
+        "roofline": mfma_roofline(flops, attn_ms, counters_for(counter_key) if counter_key else None),
+    }
+    extra = dict(cfg=cfg, gate=gate, step_ms=step_ms, flops=flops)
+    del q, k, v, qkv, out
+    torch.cuda.empty_cache()
+    return res, extra
 
 
 def bench_rope(args):
-    """The same prefill step from pre-RoPE Q and K: hifa4_quantize_qkv_rope rotates, rescales and
+    """The headline step from pre-RoPE Q and K: hifa4_quantize_qkv_rope rotates, rescales and
     quantizes Q and K (and quantizes V) in streaming passes, then the attention from the codes."""
     import torch
     import bit_quantized_flashattention_amd as hf
@@ -166,7 +232,7 @@ def bench_rope(args):
     out = torch.empty((b, hq, lq, d), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev):
         if ev is not None:
             ev[0].record(stream)
         hf.quantize_qkv_rope(q, k, v, sd, invd, cosd, sind, dims=dims, out=qkv)
@@ -176,31 +242,23 @@ def bench_rope(args):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    quant_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    step_ms = (t1 - t0) * 1e3 / args.steps
+    step_ms, gaps = timed(step, 3, args)
+    quant = [g[0] for g in gaps]
+    attn = [g[1] for g in gaps]
     flops = 4.0 * d * causal_pairs(lq, lk) * b * hq
     # algorithmic bytes of the Q, K (RoPE) and V quantizers: FP16 in, codes and scales out, the
     # tables and the Smooth-QK scales once
     elems = b * (hq + 2 * hkv) * lk * d
     q_bytes = elems * 2 + elems // 2 + elems // 32 + lk * d * 4 + 2 * hkv * d * 4
+    quant_ms = statistics.fmean(quant)
     res = {
         "workload": "%s from pre-RoPE Q/K: Q/K/V quantize with RoPE on Q and K, then attention" % cfg["name"],
-        "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "ms_per_step": round(step_ms, 4),
-        "attention_ms": round(attn_ms, 4),
-        "quantize_qkv_rope": {"us": round(quant_ms * 1e3, 1), "bytes": q_bytes,
-                             "achieved_gbs": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS},
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
+        "attention_ms": spread(attn),
+        "quantize_qkv_rope": {"us": round(quant_ms * 1e3, 1), "us_median": round(statistics.median(quant) * 1e3, 1),
+                              "us_min": round(min(quant) * 1e3, 1), "us_max": round(max(quant) * 1e3, 1),
+                              "bytes": q_bytes, "achieved_gbs": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                              "peak_gbs": HBM_PEAK_GBS},
     }
     del q, k, v, qkv, out
     torch.cuda.empty_cache()
@@ -268,7 +326,7 @@ def bench_decode(args):
     out = torch.empty((b, hq, 1, d), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev):
         if ev is not None:
             ev[0].record(stream)
         # the FP16 query is rescaled and quantized inside the split kernel
@@ -276,24 +334,16 @@ def bench_decode(args):
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    n = max(args.steps, 20)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    t0 = time.perf_counter()
-    for i in range(n):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    attn_ms = sum(a.elapsed_time(c) for a, c in evs) / n
-    step_ms = (t1 - t0) * 1e3 / n
+    step_ms, gaps = timed(step, 2, args)
+    attn = [g[0] for g in gaps]
+    attn_ms = statistics.fmean(attn)
     lk32 = -(-lk // 32) * 32
     kv_bytes = 2 * b * hkv * (lk * d // 2 + lk * d // 32)  # K-hat and V-hat codes + scales
     assert kv_bytes == b * hkv * (lk * (d // 2 + d // 32) + d * (lk32 // 2 + lk32 // 32))
     q_bytes = b * hq * d * 2 + hkv * d * 4  # FP16 query and the Smooth-QK scales
     out_bytes = b * hq * d * 2
     total = kv_bytes + q_bytes + out_bytes
+    ctr = counters_for("decode")
     res = {
         "workload": "split-KV decode B%d Hq%d/Hkv%d d%d Lk%d, 4-bit cache, %d splits" % (b, hq, hkv, d, lk, splits),
         "metric": "decode HBM GB/s",
@@ -301,47 +351,81 @@ def bench_decode(args):
         "unit": "GB/s",
         "us_per_step": round(step_ms * 1e3, 1),
         "bytes_per_step": total,
+        "kernel_ms": spread(attn),
         "roofline": {"bound": "hbm", "achieved": round(total / (attn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(total / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("decode"), "kernel_us": round(attn_ms * 1e3, 1)},
+                     "traffic": ctr.get("traffic") if ctr else None, "kernel_us": round(attn_ms * 1e3, 1)},
     }
     del qkv, ws, out, q, k, v
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(args, pre):
-    """The oracle, as it stands, timed on host cores on a bounded sample of the same workload."""
+# ---------------------------------------------------------------------------- CPU oracle baseline
+
+def _cpu_unit(job):
+    """One (batch, KV head) unit of the prefill workload on one core: the oracle quantizes the KV
+    head's K and V and its query heads, then attends sample rows until the budget is spent."""
+    from threadpoolctl import threadpool_limits
     import numpy as np
-    import torch
     from oracle import attention as A
+    with threadpool_limits(1):
+        q, k, v, s, inv, cfg, seconds, seed = job
+        d, lq, lk = cfg["d"], cfg["Lq"], cfg["Lk"]
+        t0 = time.perf_counter()
+        qq = A.quantize_qkv(q, k, v, s, inv)
+        rng = np.random.default_rng(seed)
+        flops = 0.0
+        rows_done = 0
+        hq = q.shape[1]
+        while time.perf_counter() - t0 < seconds:
+            h = int(rng.integers(hq))
+            rows = np.sort(rng.choice(lq, size=16, replace=False))
+            A.attention_head_p(qq, 0, h, rows, cfg["causal"], cfg["kv_tile"], A.P_REORDERED)
+            vis = np.minimum(lk, rows + (lk - lq) + 1) if cfg["causal"] else np.full(len(rows), lk)
+            flops += 4.0 * d * float(vis.sum())
+            rows_done += len(rows)
+        return flops, rows_done, time.perf_counter() - t0
+
+
+def cpu_baseline(args):
+    """The oracle, as it stands, on the host's cores: one process per (batch, KV head) unit of the
+    headline workload (one BLAS thread each), as many units as cores; each unit quantizes its
+    K/V head and query heads, then attends randomly drawn query rows for a fixed budget.
+    Rate = sum of the units' algorithmic FLOPs / wall time of the pool."""
+    import multiprocessing as mp
+    import numpy as np
+    import synth
     from oracle import smooth
 
-    cfg = pre["cfg"]
-    q, k, v = pre["qkv_inputs"]
-    d, lq, lk, hq, hkv = cfg["d"], cfg["Lq"], cfg["Lk"], cfg["Hq"], cfg["Hkv"]
-    qh = q[0:1, 0:1].cpu().numpy()
-    kh = k[0:1, 0:1].cpu().numpy()
-    vh = v[0:1, 0:1].cpu().numpy()
-    import synth
+    cfg = synth.config(2)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    group = cfg["Hq"] // cfg["Hkv"]
     q_cal, k_cal = synth.make_calibration(cfg)
     s, inv, _ = smooth.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
-    rng = np.random.default_rng(0)
+    jobs = []
+    b = 0
+    while len(jobs) < cores:
+        q, k, v = synth.make_qkv(cfg, batch_slice=(b, b + 1))
+        for g in range(cfg["Hkv"]):
+            if len(jobs) == cores:
+                break
+            jobs.append((np.ascontiguousarray(q[:, g * group:(g + 1) * group]), np.ascontiguousarray(k[:, g:g + 1]),
+                         np.ascontiguousarray(v[:, g:g + 1]), s[g:g + 1], inv[g:g + 1], cfg, args.cpu_seconds,
+                         1000 * b + g))
+        b += 1
+    ctx = mp.get_context("spawn")  # fresh interpreters: the workers never touch the GPU
     t0 = time.perf_counter()
-    qq = A.quantize_qkv(qh, kh, vh, s[:1], inv[:1])
-    flops = 0.0
-    rows_done = 0
-    while time.perf_counter() - t0 < args.cpu_seconds:
-        rows = np.sort(rng.choice(lq, size=16, replace=False))
-        A.attention_head_p(qq, 0, 0, rows, cfg["causal"], cfg["kv_tile"], A.P_REORDERED)
-        shift = lk - lq
-        vis = np.minimum(lk, rows + shift + 1) if cfg["causal"] else np.full(len(rows), lk)
-        flops += 4.0 * d * float(vis.sum())
-        rows_done += len(rows)
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": "%d query rows of head (0,0) of the prefill workload incl. that head's quantization; %.1f s"
-                      % (rows_done, el)}
+    with ctx.Pool(cores) as pool:
+        res = pool.map(_cpu_unit, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    flops = sum(r[0] for r in res)
+    rows = sum(r[1] for r in res)
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(wall, 2), "gflops": round(flops / wall / 1e9, 3),
+            "sample": "%d (batch, KV head) units of the headline workload in parallel (one process and one BLAS "
+                      "thread per core); each quantizes its K/V head and %d query heads, then attends randomly "
+                      "drawn query rows for %.0f s: %d rows in all" % (cores, group, args.cpu_seconds, rows)}
 
 
 def main():
@@ -351,46 +435,47 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
-    cfg_id = {"prefill": 2, "prefill-d256": 3, "prefill-L2048": 1}[args.workload]
-    pre = bench_prefill(args, cfg_id)
-    cfg = pre["cfg"]
-    attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
-    step_tflops = pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12
+    pre, ex = bench_prefill(args, 2, counter_key="prefill")
+    cfg = ex["cfg"]
     line = {
         "metric": "4-bit attention fwd TFLOP/s (+% FP4-MFMA peak); decode HBM GB/s",
-        "value": round(step_tflops, 2),
+        "value": pre["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(pre["step_ms"], 4),
+        "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4",
         "data": "synthetic",
         "config": {
-            "workload": "%s: causal=%s B%d Hq%d/Hkv%d d%d L%d, kv_tile %d, per step: K/V quantize + attention with Q quantized in-kernel"
-                        % (cfg["name"], cfg["causal"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lq"],
-                           cfg["kv_tile"]),
+            "workload": pre["workload"],
             "global_batch": cfg["B"], "seq_len": cfg["Lq"], "heads_q": cfg["Hq"], "heads_kv": cfg["Hkv"],
-            "head_dim": cfg["d"], "normalizer": "p_reordered", "smooth_qk_gate": pre["gate"],
+            "head_dim": cfg["d"], "normalizer": "p_reordered", "phat": "per 32-key block, exp16 codes",
+            "smooth_qk_gate": ex["gate"],
         },
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 4), "traffic": traffic_for("prefill") if args.workload == "prefill" else None,
-                     "kernel_ms": round(pre["attn_ms"], 4)},
+        "roofline": pre["roofline"],
+        "attention_ms": pre["attention_ms"],
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, pre)
-    del pre
-    torch.cuda.empty_cache()
-    if not args.no_rope and args.workload == "prefill":
+    if "prefill_d256" in args.leg_list:
+        line["prefill_d256"] = bench_prefill(args, 3, counter_key="prefill_d256")[0]
+    if "direct_p" in args.leg_list:
+        line["direct_p"] = bench_prefill(args, 2, phat_rule=1, counter_key="direct_p")[0]
+    if "noncausal" in args.leg_list:
+        line["noncausal"] = {"exp16": bench_prefill(args, 2, causal=False)[0],
+                             "direct_p": bench_prefill(args, 2, causal=False, phat_rule=1)[0]}
+    if "rope_prefill" in args.leg_list:
         line["rope_prefill"] = bench_rope(args)
-    if not args.no_decode:
+    if "decode" in args.leg_list:
         line["decode"] = bench_decode(args)
         line["decode"]["cache_append"] = bench_append(args)
     if args.traffic_probe:
         copy_probe()
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(line), flush=True)
 
 
