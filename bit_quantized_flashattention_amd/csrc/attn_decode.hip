@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
     }
   }
 
-  const float C = a.c_log2;
+  constexpr float C = SoftmaxC<D>::value;  // equals a.c_log2 (checked by the launcher)
   const int64_t shift = lk - 1;
 
   h2 o[CB][2];
@@ -254,6 +254,7 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  if (a.c_log2 != SoftmaxC<D>::value) return hipErrorInvalidValue;  // the kernel's constant must be the caller's C
   const int group = a.heads_q / a.heads_kv;
   dim3 grid((uint32_t)a.num_splits, (uint32_t)(a.heads_kv * ((group + 15) / 16)), (uint32_t)a.batch);
   if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1, 0>), grid, dim3(64), 0, s, a);

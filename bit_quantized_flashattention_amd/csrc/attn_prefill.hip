@@ -361,7 +361,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   LoadOp ops[Cf::kMaxLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < Cf::kMaxLoadsPerWave; i++) ops[i] = load_op<D>(wave_u + W * i, lane, (int)rows32);
-  const float C = a.c_log2;
+  constexpr float C = SoftmaxC<D>::value;  // equals a.c_log2 (checked by the launcher)
 
   // per-lane LDS offsets of this lane's MFMA operands (see the reads in the tile loop)
   const int k_lane_off = Cf::kKC + 16 * lane;
@@ -584,6 +584,7 @@ hipError_t launch2(const AttnArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch1(const AttnArgs& a, hipStream_t s) {
+  if (a.c_log2 != SoftmaxC<D>::value) return hipErrorInvalidValue;  // the kernel's constant must be the caller's C
   return a.causal ? launch2<D, true>(a, s) : launch2<D, false>(a, s);
 }
 

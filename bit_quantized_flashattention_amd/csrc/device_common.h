@@ -183,6 +183,24 @@ __device__ __forceinline__ uint32_t quantize_block32(const uint16_t* x, const fl
   return quantize_loaded32(in, s != nullptr, codes);
 }
 
+// The softmax scale in the log2 domain, C = fp32(log2(e) / sqrt(d)), as a compile-time constant
+// per head dimension: the per-score fma(S, C, offset) then takes the literal-operand form, which
+// the vector ALU issues at twice the rate of the three-register form.
+template <int D>
+struct SoftmaxC;
+template <>
+struct SoftmaxC<64> {
+  static constexpr float value = 0x1.715476p-3f;
+};
+template <>
+struct SoftmaxC<128> {
+  static constexpr float value = 0x1.0527dcp-3f;
+};
+template <>
+struct SoftmaxC<256> {
+  static constexpr float value = 0x1.715476p-4f;
+};
+
 // log2(6) rounded to the nearest FP32 (0x40257007): 6 is the largest E2M1 magnitude.
 constexpr float kLog2Six = 0x1.4ae00ep+1f;
 
@@ -270,7 +288,9 @@ __device__ __forceinline__ PhatScale phat_scale(float emax, float C, float mm) {
   PhatScale p;
   const float v = __builtin_fmaf(emax, C, -mm);
   p.e = DIRECT ? direct_exponent(v) : tile_exponent(v);
-  p.neg_big_m = -(mm + p.e);
+  // held negated in a register: a negation folded into the per-score fma as an operand modifier
+  // would force its slower three-register form
+  p.neg_big_m = keep_f32(-(mm + p.e));
   return p;
 }
 

@@ -60,7 +60,7 @@ struct AttnArgs {
   int32_t num_splits;
   int32_t tiles_per_split;
   int32_t heads_per_wg;  // prefill: query heads served by one work-group (set by the launcher)
-  float c_log2;         // fp32(log2(e) / sqrt(d))
+  float c_log2;         // fp32(log2(e) / sqrt(d)); the kernels use the same value as a constant per d
 };
 
 struct QuantRopeArgs {
