@@ -450,9 +450,14 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
         if (k0 + bc - 1 < lim) lim = k0 + bc - 1;
         if (q >= lq) lim = -1;
         const int rel = lim - kb;  // key offset s_key(k) of the lane's block is visible iff <= rel
+        // the mask as arithmetic (no compare and select, whose condition register costs wait
+        // states): min(s, +inf) keeps a visible score, min(s, -inf) masks one; the sign of
+        // rel - s_key(k) + 1/2 (never 0) tells which, and times +inf it is that bound
+        const float relf = (float)(rel < -1 ? -1 : (rel > 31 ? 31 : rel));
 #pragma unroll
         for (int k = 0; k < 32; k++) {
-          s[k] = (s_key(k) <= rel) ? s[k] : -INFINITY;
+          const float lim_k = (relf + (0.5f - (float)s_key(k))) * INFINITY;
+          s[k] = min_nn(s[k], lim_k);
           bmax = fmaxf(bmax, s[k]);
         }
       }

@@ -302,6 +302,13 @@ __device__ __forceinline__ float max_nn(float a, float b) {
   return r;
 }
 
+// min of two FP32 values that are never NaN, as one v_min_f32 (see max_nn)
+__device__ __forceinline__ float min_nn(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   RowStep r;
   r.m_new = max_nn(m, __builtin_ceilf(rmax * C));

@@ -3,7 +3,8 @@
 Each workload is generated on the GPU at full size, calibrated by the library, quantized and
 attended by the HIP path in one launch each.  The oracle then quantizes sampled (batch, head)
 slices of the same FP16 inputs (codes and scales must match those slices of the GPU output bit
-for bit) and computes query rows (max |d| <= 2e-3 * RMS of the oracle rows):
+for bit) and computes query rows, which must equal the GPU's bit for bit (the tolerance check
+max |d| <= 2e-3 * RMS is reported too):
 * every row of one full (batch, head) of each prefill workload, so every tile class the kernel
   has (interior, causal diagonal, ragged) is compared at full size;
 * one row from every 128-row query block of further heads;
@@ -102,13 +103,15 @@ def run_full(cfg_id, heads, normalizer=A.P_REORDERED):
         got = out[b, h].cpu().numpy()[rows]
         n_rows += len(rows)
         if lq > 1:
-            compare_out(got, want, "full config %d b%d h%d %s (%d rows)"
-                        % (cfg_id, b, h, "all rows" if all_rows else "a row per 128-row block", len(rows)))
+            _, ndiff = compare_out(got, want, "full config %d b%d h%d %s (%d rows)"
+                                   % (cfg_id, b, h, "all rows" if all_rows else "a row per 128-row block", len(rows)))
+            assert ndiff == 0, "config %d b%d h%d: %d outputs differ from the oracle" % (cfg_id, b, h, ndiff)
         else:
             gots.append(got)
             wants.append(want)
     if gots:  # decode: one query row per head, compared together
-        compare_out(np.concatenate(gots), np.concatenate(wants), "full config %d, %d query heads" % (cfg_id, len(gots)))
+        _, ndiff = compare_out(np.concatenate(gots), np.concatenate(wants), "full config %d, %d query heads" % (cfg_id, len(gots)))
+        assert ndiff == 0, "config %d: %d outputs differ from the oracle" % (cfg_id, ndiff)
     print("config %d: %d rows compared; inexact sums (oracle): scores %d, PV %d of %d, l %d"
           % (cfg_id, n_rows, totals[0], totals[1], totals[3], totals[2]), flush=True)
 
