@@ -1,9 +1,9 @@
 """Smooth-QK: calibration-static per-channel rescaling of Q and K after RoPE.
 
-[HiFA4] Abstract: Smooth-QK is an equivalent per-channel rescaling of Q and K
-applied after RoPE that moves quantization difficulty from K to Q; the scale
-factors are computed once from a small offline calibration set, and at
-inference only a fusible element-wise scaling remains.  The abstract also
+[HiFA4] Abstract: Smooth-QK rescales Q and K channel by channel after RoPE,
+leaving QK^T unchanged, so that the hard-to-quantize outliers of K move into
+Q; the factors are fixed ahead of time from a little calibration data, so
+inference adds only an element-wise multiply that fuses into the quantizer.  The abstract also
 names an applicability gate that turns Smooth-QK off for some models and a
 "mild smoothing" setting for Gemma2-9B, without giving formulas.
 

@@ -6,12 +6,13 @@ factor; the abstract measures the per-tile error epsilon = sum(P-hat)/sum(P) - 1
 probability-mass loss, and contrasts HiFA4 with direct 4-bit quantization.  This test runs the
 full workload through the C ABI, P-Reordered and inconsistent with per-(16-row block, tile)
 statistics, plus the same two without Smooth-QK (no smoothing + inconsistent is the direct
-formulation), HiFA4 with the OCP floor block-scale rule and HiFA4 with the round-to-nearest FP16
-running max, and reports:
+formulation), HiFA4 with the OCP floor block-scale rule, HiFA4 with the round-to-nearest FP16
+running max, HiFA4 with one P-hat scale per (row, key tile) instead of per (row, 32-key block),
+and HiFA4 with Direct-P codes, and reports:
 
 * epsilon over all visited tiles (median, mean, p5, p95, fraction below 0); m does not depend on
   l, so both runs must produce identical tile sums;
-* the error of the six outputs against unquantized FP32 softmax attention
+* the error of the eight outputs against unquantized FP32 softmax attention
   (oracle.reference_fp32 on the original FP16 inputs) on sampled heads.
 
 The magnitude of epsilon has no value on the pages for synthetic inputs (parity unpinned); the
@@ -86,9 +87,16 @@ def test_accuracy_report_batched_prefill():
     # the round-to-nearest FP16 running max in place of the integer one (same codes)
     runs["nearest_running_max"] = (hf.attention_fwd(res, dims, True, A.P_REORDERED, cfg["kv_tile"],
                                                     max_rule=hf.MAX_NEAREST16), None)
+    # P-hat with one scale per (row, key tile) instead of per (row, 32-key block): what the
+    # block format buys
+    runs["phat_per_tile_scale"] = (hf.attention_fwd(res, dims, True, A.P_REORDERED, cfg["kv_tile"],
+                                                    phat_scale=hf.PHAT_TILE), None)
+    # Direct-P codes (no exponential; the FA4 prior art) with the per-block scale
+    runs["direct_p_codes"] = (hf.attention_fwd(res, dims, True, A.P_REORDERED, cfg["kv_tile"],
+                                               phat_rule=hf.PHAT_DIRECT), None)
     torch.cuda.synchronize()
     err = {"p_reordered": [], "inconsistent": [], "no_smooth_p_reordered": [], "direct": [], "floor_scale_rule": [],
-           "nearest_running_max": []}
+           "nearest_running_max": [], "phat_per_tile_scale": [], "direct_p_codes": []}
     heads = [(0, 0), (2, 9), (5, 22), (7, 31)]
     group = hq // hkv
     for (b, h) in heads:
