@@ -31,9 +31,10 @@ WORKERS = max(1, min(len(os.sched_getaffinity(0)), 16))
 
 
 def _oracle_rows(job):
-    qq, h, rows, causal, kv_tile, normalizer, splits = job
+    qq, h, rows, causal, kv_tile, normalizer, splits, phat_rule = job
     diag = A.Diag()
-    out = A.attention_head_p(qq, 0, h, rows, causal, kv_tile, normalizer, num_splits=splits, diag=diag)
+    out = A.attention_head_p(qq, 0, h, rows, causal, kv_tile, normalizer, num_splits=splits, diag=diag,
+                             phat_rule=phat_rule)
     return out, (diag.inexact_s, diag.inexact_pv, diag.inexact_l, diag.total_pv)
 
 
@@ -45,13 +46,18 @@ def _block_rows(rng, lq, block=128):
     return np.array(sorted(rows))
 
 
-def run_full(cfg_id, heads, normalizer=A.P_REORDERED):
-    """heads: list of (batch, query head, all_rows); all_rows False takes a row per 128-row block."""
+def run_full(cfg_id, heads, normalizer=A.P_REORDERED, causal=None, phat_rule=A.PHAT_EXP16):
+    """heads: list of (batch, query head, all_rows); all_rows False takes a row per 128-row block.
+    causal overrides the workload's mask (the bench's non-causal legs); phat_rule selects the
+    P-hat code rule (the bench's Direct-P legs)."""
     import torch
-    cfg = synth.config(cfg_id)
+    cfg = dict(synth.config(cfg_id))
+    if causal is not None:
+        cfg["causal"] = causal
     b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
     group = hq // hkv
-    print("case full-size config", cfg_id, cfg["name"], "normalizer", normalizer, flush=True)
+    print("case full-size config", cfg_id, cfg["name"], "normalizer", normalizer, "causal", cfg["causal"],
+          "phat_rule", phat_rule, flush=True)
     q, k, v = synth.make_qkv_device(cfg)
     q_cal, k_cal = synth.make_calibration(cfg)
     s, inv, gate = hf.calibrate(q_cal, k_cal, cfg["alpha"], 4.0)
@@ -61,10 +67,10 @@ def run_full(cfg_id, heads, normalizer=A.P_REORDERED):
     dims = hf.make_dims(b_n, hq, hkv, d, lq, lk)
     res = hf.quantize_qkv(q, k, v, torch.from_numpy(s).cuda(), torch.from_numpy(inv).cuda(), dims=dims)
     splits = hf.decode_num_splits(dims, hf.make_opts(cfg["causal"], normalizer, cfg["kv_tile"], 0))
-    out = hf.attention_fwd(res, dims, cfg["causal"], normalizer, cfg["kv_tile"])
+    out = hf.attention_fwd(res, dims, cfg["causal"], normalizer, cfg["kv_tile"], phat_rule=phat_rule)
     # the launch bench.py times: K-hat, V-hat from the quantizer, Q quantized inside the kernel
     out16 = hf.attention_fwd(res, dims, cfg["causal"], normalizer, cfg["kv_tile"],
-                             q16=(q, torch.from_numpy(s).cuda()))
+                             q16=(q, torch.from_numpy(s).cuda()), phat_rule=phat_rule)
     torch.cuda.synchronize()
     assert torch.equal(out16.view(torch.int16), out.view(torch.int16)), "fused-Q output differs"
     rng = np.random.default_rng(7000 + cfg_id)
@@ -89,7 +95,7 @@ def run_full(cfg_id, heads, normalizer=A.P_REORDERED):
             rows = np.arange(lq) if all_rows else _block_rows(rng, lq)
             chunks = [c for c in np.array_split(rows, max(1, min(len(rows), 4 * WORKERS))) if len(c)]
             for c in chunks:
-                jobs.append((qq, hl, c, cfg["causal"], cfg["kv_tile"], normalizer, splits if lq == 1 else 1))
+                jobs.append((qq, hl, c, cfg["causal"], cfg["kv_tile"], normalizer, splits if lq == 1 else 1, phat_rule))
                 meta.append((b, h, all_rows, c))
     with mp.get_context("spawn").Pool(WORKERS) as pool:
         results = pool.map(_oracle_rows, jobs, chunksize=1)
@@ -123,6 +129,17 @@ def test_full_qwen_shaped_L2048():
 @pytest.mark.parametrize("normalizer", [A.P_REORDERED, A.INCONSISTENT])
 def test_full_batched_B8_L4096(normalizer):
     run_full(2, [(3, 17, True), (0, 0, False), (7, 31, False)], normalizer)
+
+
+def test_full_batched_B8_L4096_direct_p():
+    """The bench's direct_p leg: Direct-P codes at the batched workload."""
+    run_full(2, [(5, 9, True), (1, 30, False)], phat_rule=A.PHAT_DIRECT)
+
+
+@pytest.mark.parametrize("phat_rule", [A.PHAT_EXP16, A.PHAT_DIRECT])
+def test_full_batched_B8_L4096_noncausal(phat_rule):
+    """The bench's non-causal legs (both code rules): a row per 128-row block of two heads."""
+    run_full(2, [(2, 6, False), (6, 27, False)], causal=False, phat_rule=phat_rule)
 
 
 def test_full_gemma_shaped_d256_L8192():
