@@ -66,6 +66,24 @@ def _compile(src):
     return obj
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "mfma_probe", "mfma_probe.hip")
+PROBE_OUT = os.path.join(ROOT, "tests", "mfma_probe", "libmfmaprobe.so")
+
+
+def build_test_probe(verbose=False):
+    """The GPU tests' instruction probe (tests/mfma_probe): one scaled FP4 MFMA per wave on buffer
+    operands.  Test infrastructure, not part of libhifa4.so."""
+    tmp = PROBE_OUT + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE_OUT)
+    if verbose:
+        print("built", PROBE_OUT)
+    return PROBE_OUT
+
+
 def build(verbose=False):
     os.makedirs(OBJDIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
@@ -78,6 +96,8 @@ def build(verbose=False):
     os.replace(tmp, OUT)
     if verbose:
         print("built", OUT)
+    if os.path.exists(PROBE_SRC):
+        build_test_probe(verbose)
     return OUT
 
 
