@@ -233,6 +233,14 @@ __device__ __forceinline__ uint32_t cvt_u32_sat(float y) {
   return r;
 }
 
+// float -> int32 with the hardware conversion's rules: NaN gives 0, out-of-range values (and
+// +-inf) saturate (the C cast leaves all of these undefined)
+__device__ __forceinline__ int cvt_i32_sat(float y) {
+  int r;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(y));
+  return r;
+}
+
 // rn16(2^x) of both FP16 halves of h.  v_exp_f16 is correctly rounded on every FP16 input;
 // the SDWA form writes the high half and keeps the low one, so no pack is needed.  A
 // transcendental result is not forwarded to the next instruction: the SDWA form reads the low
@@ -271,7 +279,7 @@ __device__ __forceinline__ float keep_f32(float x) {
 // rmax (-inf if none) and the running max m (-inf before the first visible key).
 struct RowStep {
   float m_new;      // integer running max ceil(fp32(max S * C)), exact in FP16
-  _Float16 alpha;   // rn16(2^(m - m_new)), 0 while m = -inf: the FP16 rescale of O and l
+  _Float16 alpha;   // rn16(2^(m - m_new)), the FP16 rescale of O and l (see row_step)
   float mm;         // m_new, or a finite stand-in below every real m while m_new = -inf
 };
 
@@ -312,11 +320,13 @@ __device__ __forceinline__ float min_nn(float a, float b) {
 __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
   RowStep r;
   r.m_new = max_nn(m, __builtin_ceilf(rmax * C));
-  // 2^(m - m_new) straight in FP16: exact down to 2^-24; below that (rn16 gives 0, 2^-25 being
-  // a tie to even) and while m = -inf (d = -inf or NaN) the exponent -64 gives 0
+  // 2^(m - m_new) straight in FP16: exact down to 2^-24; below that the result underflows to 0
+  // (2^-25 is a tie to even), and so it does for m = -inf (d = -inf saturates).  While no key of
+  // the row has been visible (m = m_new = -inf, d = NaN, converted to 0) alpha is 1, which
+  // multiplies the row's zero state: the same state as alpha = 0.  No compare and select: a
+  // select on the condition register issues far slower than this arithmetic
   const float d = m - r.m_new;
-  const int dm = d >= -24.0f ? (int)d : -64;
-  r.alpha = __builtin_ldexpf16((_Float16)1.0f, dm);
+  r.alpha = __builtin_ldexpf16((_Float16)1.0f, cvt_i32_sat(d));
   // m_new = -inf only for a row with no visible key yet: any finite stand-in below every real
   // m keeps e = -127 and every code 0
   r.mm = max_nn(r.m_new, -0x1p100f);
