@@ -546,11 +546,25 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
     __syncthreads();
   }
 
-  // ---- epilogue: out = fp16(O / l); register i of block cb holds channel 16 cb + 4 g + i
-  const int q = q0 + col;
-  if (!wave_live || q >= lq) return;
-  uint16_t* out = a.out + ((int64_t)b * a.heads_q + h) * (int64_t)lq * D;
-  write_out_row<CB>(out + (int64_t)q * D + 4 * g, o, (float)l);
+  // ---- epilogue: out = fp16(O / l); register i of block cb holds channel 16 cb + 4 g + i.  The
+  // last barrier of the tile loop has freed the LDS ring: each wave stages its 16 x D output tile
+  // there (rows padded by 16 bytes, so the 16 rows of a store do not share banks) and stores it
+  // back row-contiguous, 1 KB per store instruction, instead of scattering 32-byte pieces of 16
+  // rows from every store
+  if (!wave_live) return;
+  constexpr int kRowBytes = 2 * D + 16;
+  static_assert(W * 16 * kRowBytes <= kStages * Cf::kStageBytes, "output staging fits the LDS ring");
+  uint8_t* stile = smem + wave * 16 * kRowBytes;
+  write_out_row<CB>(stile + col * kRowBytes + 8 * g, o, (float)l);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes have completed
+  uint16_t* out = a.out + (((int64_t)b * a.heads_q + h) * (int64_t)lq + q0) * D;
+  constexpr int kChunks = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < 16 * kChunks / 64; i++) {
+    const int c = 64 * i + lane, r = c / kChunks, cc = c % kChunks;
+    const uint4 val = *reinterpret_cast<const uint4*>(stile + r * kRowBytes + 16 * cc);
+    if (q0 + r < lq) *reinterpret_cast<uint4*>(out + (int64_t)r * D + 8 * cc) = val;
+  }
 }
 
 int gcd_int(int x, int y) {

@@ -453,8 +453,9 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
 }
 
 // Writes one query's output row fp16(O / l) from the FP16 state of CB channel blocks: register i
-// (i = 0..3) of block cb holds channel 16 cb + 4 g + i, so each block gives 4 adjacent channels;
-// dst points at channel 4 g of the row.
+// (i = 0..3) of block cb holds channel 16 cb + 4 g + i, so each block gives 4 adjacent channels
+// (8 bytes); dst points at channel 4 g of the row (a row of LDS: the prefill stages its output
+// tile there and stores it row-contiguous).
 //
 // The quotient: fp16(x / l) for FP16 values x and l > 0 equals the FP16 rounding of the IEEE
 // FP32 quotient.  Here q = x r with r ~ 1/l (hardware reciprocal, ~1 ulp) is corrected once with
@@ -471,7 +472,7 @@ __device__ __forceinline__ float quot_h(float x, float l, float r) {
 }
 
 template <int CB>
-__device__ __forceinline__ void write_out_row(uint16_t* dst, const h2 (*o)[2], float l) {
+__device__ __forceinline__ void write_out_row(uint8_t* dst, const h2 (*o)[2], float l) {
   const float r = __builtin_amdgcn_rcpf(l);
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
@@ -482,7 +483,7 @@ __device__ __forceinline__ void write_out_row(uint16_t* dst, const h2 (*o)[2], f
       const float x1 = quot_h((float)o[cb][j][1], l, r);
       w[j] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
     }
-    *reinterpret_cast<uint2*>(dst + 16 * cb) = make_uint2(w[0], w[1]);
+    *reinterpret_cast<uint2*>(dst + 32 * cb) = make_uint2(w[0], w[1]);
   }
 }
 
