@@ -71,8 +71,9 @@ PROBE_OUT = os.path.join(ROOT, "tests", "mfma_probe", "libmfmaprobe.so")
 
 
 def build_test_probe(verbose=False):
-    """The GPU tests' instruction probe (tests/mfma_probe): one scaled FP4 MFMA per wave on buffer
-    operands.  Test infrastructure, not part of libhifa4.so."""
+    """The GPU tests' probes (tests/mfma_probe): one scaled FP4 MFMA per wave on buffer operands,
+    and the exhaustive check of the output quotient.  Test infrastructure, not part of
+    libhifa4.so."""
     tmp = PROBE_OUT + ".tmp"
     cmd = [HIPCC] + FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -245,8 +245,9 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
     const float a2 = __builtin_ldexpf(1.0f, (int)(ms - mn));
     const float mo = a2 * os;
     const float ml = a2 * ls;
-    o = (float)(_Float16)__builtin_fmaf(a1, o, mo);
-    l = (float)(_Float16)__builtin_fmaf(a1, l, ml);
+    // each fma is rounded to FP32 and then to FP16 (keep_f32: not fused into one FP16 rounding)
+    o = (float)(_Float16)keep_f32(__builtin_fmaf(a1, o, mo));
+    l = (float)(_Float16)keep_f32(__builtin_fmaf(a1, l, ml));
     m = mn;
   }
   a.out[bh * D + ch] = __builtin_bit_cast(uint16_t, (_Float16)(o / l));

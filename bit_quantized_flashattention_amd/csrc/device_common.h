@@ -339,7 +339,8 @@ __device__ __forceinline__ RowStep row_step(float rmax, float m, float C) {
 // gives 0 anyway); m_new + e is rounded once to FP32 (phat_scale).
 __device__ __forceinline__ RowStep row_step_nearest16(float rmax, float m, float C) {
   RowStep r;
-  r.m_new = max_nn(m, (float)(_Float16)(rmax * C));
+  // the product is rounded to FP32 first (keep_f32: not fused into one rounding to FP16)
+  r.m_new = max_nn(m, (float)(_Float16)keep_f32(rmax * C));
   const float d = m - r.m_new;
   const uint32_t a2 = exp2_h2(pack_h2(d, d));
   r.alpha = d >= -30.0f ? __builtin_bit_cast(h2, a2)[0] : (_Float16)0.0f;
@@ -457,18 +458,27 @@ __device__ __forceinline__ void state_update(h2* o, _Float16 alpha, const v4f& p
 // (8 bytes); dst points at channel 4 g of the row (a row of LDS: the prefill stages its output
 // tile there and stores it row-contiguous).
 //
-// The quotient: fp16(x / l) for FP16 values x and l > 0 equals the FP16 rounding of the IEEE
-// FP32 quotient.  Here q = x r with r ~ 1/l (hardware reciprocal, ~1 ulp) is corrected once with
-// the exact residual fma(-l, q, x), which leaves q within 0.5 ulp (FP32) plus O(2^-45) of x / l;
-// a quotient of two FP16 values is never an FP16 rounding midpoint (a midpoint has 12
-// significant bits) and stays at least 2^-22 (relative) away from one, so both round to the same
-// FP16 value.  The residual is taken negated, d = fma(l, q, -x) (the same rounding of the same
-// exact value with the opposite sign), and the correction is q - d r: then x = -0 keeps its sign
-// through every step (q = -0, d = +0, -0 * r + -0 = -0) without a separate sign copy.
+// The quotient: fp16(x / l) for FP16 values x and l > 0.  q = x r with r ~ 1/l (hardware
+// reciprocal, ~1 ulp) is corrected once with the exact residual, which leaves the corrected value
+// within about 2^-45 (relative) of x / l; it is then rounded to FP32 and only then to FP16.  A
+// quotient of two FP16 values that is an FP16 rounding tie (possible only in the subnormal range,
+// e.g. 9 * 2^-24 / 6) has at most 12 significant bits, so the FP32 rounding returns it exactly and
+// the conversion breaks the tie to even; any other quotient lies farther from every tie than the
+// FP32 rounding moves it.  tests/test_gpu_quotient.py checks every pair of finite FP16 x and
+// positive finite FP16 l.  The residual is taken negated, d = fma(l, q, -x) (the same rounding of
+// the same exact value with the opposite sign), and the correction is q - d r: then x = -0 keeps
+// its sign through every step (q = -0, d = +0, -0 * r + -0 = -0) without a separate sign copy.
 __device__ __forceinline__ float quot_h(float x, float l, float r) {
   const float q = x * r;
   const float d = __builtin_fmaf(l, q, -x);
   return __builtin_fmaf(-d, r, q);
+}
+
+// fp16(x / l) with r = rcp(l): the FP32 quotient is kept as it is (keep_f32), so the compiler
+// cannot fuse the last fma with the conversion into a mixed-precision fma that rounds once to
+// FP16 (that form rounds exact ties in the wrong direction)
+__device__ __forceinline__ _Float16 quot_h16(float x, float l, float r) {
+  return (_Float16)keep_f32(quot_h(x, l, r));
 }
 
 template <int CB>
@@ -479,9 +489,7 @@ __device__ __forceinline__ void write_out_row(uint8_t* dst, const h2 (*o)[2], fl
     uint32_t w[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-      const float x0 = quot_h((float)o[cb][j][0], l, r);
-      const float x1 = quot_h((float)o[cb][j][1], l, r);
-      w[j] = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+      w[j] = __builtin_bit_cast(uint32_t, h2{quot_h16((float)o[cb][j][0], l, r), quot_h16((float)o[cb][j][1], l, r)});
     }
     *reinterpret_cast<uint2*>(dst + 32 * cb) = make_uint2(w[0], w[1]);
   }
