@@ -12,6 +12,10 @@
 // quot_probe_run: the library's output quotient (hifa4::quot_h16 of device_common.h, used by the
 // prefill epilogue) against the correctly rounded FP16 quotient, for every finite FP16 x and
 // every positive finite FP16 l.
+//
+// prim_probe_run: the library's elementwise P-hat helpers (device_common.h) on given FP16 inputs:
+// hifa4::exp2_h2 (both halves) and the E2M1 conversions of FP16 (hifa4::cvt_fp4x2_h) and FP32
+// (hifa4::cvt_fp4x2) values at scale 1, for a GPU test to compare with the oracle.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -100,5 +104,30 @@ __global__ __launch_bounds__(256) void quot_probe_kernel(unsigned long long* cou
 extern "C" int quot_probe_run(void* counts, void* first, void* stream) {
   hipLaunchKernelGGL(quot_probe_kernel, dim3((0x7BFFu + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                      (unsigned long long*)counts, (uint32_t*)first);
+  return (int)hipGetLastError();
+}
+
+// thread i: h[i] in both halves of a dword; exp_out[2 i], exp_out[2 i + 1] = the two halves of
+// exp2_h2; code16[i] = the byte of cvt_fp4x2_h (low nibble from the low half); code32[i] = the
+// byte of cvt_fp4x2 on the FP32 value, scale 1
+__global__ __launch_bounds__(256) void prim_probe_kernel(const uint16_t* h, uint16_t* exp_out, uint8_t* code16,
+                                                         uint8_t* code32, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t v = h[i];
+  const uint32_t packed = v | (v << 16);
+  const uint32_t e = hifa4::exp2_h2(packed);
+  exp_out[2 * i] = (uint16_t)(e & 0xFFFF);
+  exp_out[2 * i + 1] = (uint16_t)(e >> 16);
+  code16[i] = (uint8_t)(hifa4::cvt_fp4x2_h<0>(0u, packed) & 0xFF);
+  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)v);
+  code32[i] = (uint8_t)(hifa4::cvt_fp4x2<0>(0u, f, f, 1.0f) & 0xFF);
+}
+
+// device pointers: h [n] FP16 bits, exp_out [2 n], code16 [n], code32 [n]
+extern "C" int prim_probe_run(const void* h, void* exp_out, void* code16, void* code32, int n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(prim_probe_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)h, (uint16_t*)exp_out, (uint8_t*)code16, (uint8_t*)code32, n);
   return (int)hipGetLastError();
 }
