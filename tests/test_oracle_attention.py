@@ -452,3 +452,14 @@ def test_reference_fp32_matches_float64_textbook():
     v = rng.standard_normal((90, 64))
     got = A.reference_fp32(q, k, v, True)
     assert np.allclose(got, softmax_attention(q, k, v, True), rtol=1e-4, atol=1e-5)
+
+
+def test_epilogue_breaks_subnormal_quotient_ties_to_even():
+    """R13: out = fp16 of the IEEE FP32 quotient.  Quotients of two FP16 values that are exact FP16
+    ties exist only in the subnormal range: 9 * 2^-24 / 6 = 1.5 * 2^-24 goes to 2 * 2^-24 (even),
+    and 15 * 2^-24 / 6 = 2.5 * 2^-24 to 2 * 2^-24; a non-tie neighbour rounds to nearest."""
+    tiny = 2.0 ** -24
+    o = np.array([[9 * tiny, 15 * tiny, 7 * tiny, -9 * tiny]], dtype=np.float16)
+    st = A.State(np.zeros(1, dtype=np.float32), np.array([6.0], dtype=np.float16), o)
+    out = A.finish(st).astype(np.float64)[0]
+    assert list(out / tiny) == [2.0, 2.0, 1.0, -2.0]
