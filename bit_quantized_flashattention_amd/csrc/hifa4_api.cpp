@@ -217,18 +217,23 @@ hifa4_status hifa4_quantize_qkv_rule(const hifa4_dims* dims, int32_t scale_rule,
     hipError_t e = hifa4::launch_quantize_rows(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
   }
+  const hifa4::QuantRowsArgs ka{(const uint16_t*)k, inv_s, (int64_t)dims->batch * dims->heads_kv * dims->len_kv,
+                                dims->len_kv, round32(dims->len_kv), dims->heads_kv, 1, dims->head_dim, 1,
+                                (uint8_t*)k_codes, (uint8_t*)k_scales, scale_rule};
+  const hifa4::QuantVtArgs va{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
+                              round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales,
+                              scale_rule};
+  if (k && v) {
+    hipError_t e = hifa4::launch_quantize_kv(ka, va, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k, v: ") + hipGetErrorString(e));
+    return ok();
+  }
   if (k) {
-    hifa4::QuantRowsArgs a{(const uint16_t*)k, inv_s, (int64_t)dims->batch * dims->heads_kv * dims->len_kv,
-                           dims->len_kv, round32(dims->len_kv), dims->heads_kv, 1, dims->head_dim, 1,
-                           (uint8_t*)k_codes, (uint8_t*)k_scales, scale_rule};
-    hipError_t e = hifa4::launch_quantize_rows(a, stream);
+    hipError_t e = hifa4::launch_quantize_rows(ka, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
   }
   if (v) {
-    hifa4::QuantVtArgs a{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
-                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales,
-                         scale_rule};
-    hipError_t e = hifa4::launch_quantize_vt(a, stream);
+    hipError_t e = hifa4::launch_quantize_vt(va, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize v: ") + hipGetErrorString(e));
   }
   return ok();

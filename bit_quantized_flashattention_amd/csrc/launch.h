@@ -103,6 +103,8 @@ hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
 hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
 hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s);
 hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
+// K-hat rows (block planes) and V-hat tiles of one (K, V) pair in one launch
+hipError_t launch_quantize_kv(const QuantRowsArgs& ka, const QuantVtArgs& va, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 

@@ -15,12 +15,12 @@ namespace hifa4 {
 // (batch, head), its Smooth-QK scale row is staged in LDS once instead of every thread reading
 // its 128 bytes of scales through the vector memory path.
 template <int D, bool PLANES>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
+__device__ __forceinline__ void quantize_rows_block(const QuantRowsArgs& a, int64_t block) {
   constexpr int NB = D / kBlock;
   __shared__ __attribute__((aligned(16))) float s_row[D];
   const int64_t n_rows = PLANES ? a.rows / a.len * a.len32 : a.rows;
   const int64_t n_items = n_rows * NB;
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x;
+  const int64_t t0 = block * blockDim.x;
   const int64_t t = t0 + threadIdx.x;
   // (batch, head) index of the work-group's first and last row; uniform across the group
   const int64_t t_last = (t0 + blockDim.x < n_items ? t0 + blockDim.x : n_items) - 1;
@@ -64,6 +64,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   *scale_dst = (uint8_t)e8;
 }
 
+template <int D, bool PLANES>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
+  quantize_rows_block<D, PLANES>(a, blockIdx.x);
+}
+
 // V: blocks run along tokens, so a work-group stages one 32-token block x d channels in LDS and
 // each thread quantizes (channel, block) items.  The output is block-major (for each 32-token
 // block, all channels), so consecutive threads write consecutive 16-byte cells.  Small LDS tiles
@@ -73,13 +78,12 @@ template <int D>
 constexpr int vt_tokens() { return 32; }
 
 template <int D>
-__global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
+__device__ __forceinline__ void quantize_vt_block(const QuantVtArgs& a, int64_t tile_idx, int64_t bh) {
   constexpr int TOK = vt_tokens<D>();
   constexpr int NBT = TOK / kBlock;  // 32-token blocks per tile
   constexpr int ROW = D + 8;  // FP16 elements per LDS row (padding breaks bank aliasing)
   __shared__ _Float16 tile[TOK * ROW];
-  const int64_t bh = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * TOK;
+  const int64_t t0 = tile_idx * TOK;
   const uint16_t* src = a.v + bh * a.len * D;
   constexpr int CPR = D / 8;  // 16-byte chunks per token row
   for (int c = threadIdx.x; c < TOK * CPR; c += blockDim.x) {
@@ -113,6 +117,26 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
     const int64_t blk_row = (bh * (a.len32 / kBlock) + t0 / kBlock + jb) * D;
     *reinterpret_cast<uint4*>(a.codes + (blk_row + ch) * 16) = out;
     a.scales[blk_row + (D / 16) * (ch % 16) + ch / 16] = (uint8_t)(e + 127);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_vt_kernel(QuantVtArgs a) {
+  quantize_vt_block<D>(a, blockIdx.x, blockIdx.y);
+}
+
+// K-hat (block planes) and V-hat in one launch: work-groups [0, k_blocks) quantize K rows, the
+// rest V tiles (tile fastest), so the K tail and the V start overlap instead of being separated
+// by a kernel boundary.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kv_kernel(QuantRowsArgs ka, QuantVtArgs va, int64_t k_blocks,
+                                                          int64_t v_tiles) {
+  const int64_t blk = blockIdx.x;
+  if (blk < k_blocks) {
+    quantize_rows_block<D, true>(ka, blk);
+  } else {
+    const int64_t vb = blk - k_blocks;
+    quantize_vt_block<D>(va, vb % v_tiles, vb / v_tiles);
   }
 }
 
@@ -318,6 +342,27 @@ static hipError_t quant_vt_d(const QuantVtArgs& a, hipStream_t s) {
   const int64_t tiles = (a.len + vt_tokens<D>() - 1) / vt_tokens<D>();
   hipLaunchKernelGGL(quantize_vt_kernel<D>, dim3((uint32_t)tiles, (uint32_t)a.bh), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t quant_kv_d(const QuantRowsArgs& ka, const QuantVtArgs& va, hipStream_t s) {
+  const int64_t k_items = ka.rows / ka.len * ka.len32 * (D / kBlock);
+  const int64_t k_blocks = (k_items + 255) / 256;
+  const int64_t v_tiles = (va.len + vt_tokens<D>() - 1) / vt_tokens<D>();
+  const int64_t blocks = k_blocks + v_tiles * va.bh;
+  if (blocks >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_kv_kernel<D>, dim3((uint32_t)blocks), dim3(256), 0, s, ka, va, k_blocks, v_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_kv(const QuantRowsArgs& ka, const QuantVtArgs& va, hipStream_t s) {
+  if (!ka.block_planes || ka.d != va.d) return hipErrorInvalidValue;
+  switch (ka.d) {
+    case 64: return quant_kv_d<64>(ka, va, s);
+    case 128: return quant_kv_d<128>(ka, va, s);
+    case 256: return quant_kv_d<256>(ka, va, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s) {
