@@ -185,15 +185,18 @@ def bench_prefill(args, cfg_id, causal=None, phat_rule=0, counter_key=None):
 
     def step(ev):
         # K-hat, V-hat from the quantizer; Q is rescaled and quantized inside the attention kernel
-        hf.quantize_qkv(None, k, v, sd, invd, dims=dims, out=qkv)
         if ev is not None:
             ev[0].record(stream)
-        hf.attention_fwd(qkv, dims, causal, hf.P_REORDERED, cfg["kv_tile"], out=out, q16=(q, sd), phat_rule=phat_rule)
+        hf.quantize_qkv(None, k, v, sd, invd, dims=dims, out=qkv)
         if ev is not None:
             ev[1].record(stream)
+        hf.attention_fwd(qkv, dims, causal, hf.P_REORDERED, cfg["kv_tile"], out=out, q16=(q, sd), phat_rule=phat_rule)
+        if ev is not None:
+            ev[2].record(stream)
 
-    step_ms, gaps = timed(step, 2, args)
-    attn = [g[0] for g in gaps]
+    step_ms, gaps = timed(step, 3, args)
+    quant = [g[0] for g in gaps]
+    attn = [g[1] for g in gaps]
     attn_ms = statistics.fmean(attn)
     pairs = causal_pairs(lq, lk) if causal else lq * lk
     flops = 4.0 * d * pairs * b * hq
@@ -203,6 +206,7 @@ def bench_prefill(args, cfg_id, causal=None, phat_rule=0, counter_key=None):
                        "Direct-P codes" if phat_rule else "exp16 codes, one scale per 32-key block"),
         "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
         "attention_ms": spread(attn),
+        "quantize_kv_ms": spread(quant),
         "roofline": mfma_roofline(flops, attn_ms, counters_for(counter_key) if counter_key else None),
     }
     extra = dict(cfg=cfg, gate=gate, step_ms=step_ms, flops=flops)
@@ -458,6 +462,7 @@ def main():
         },
         "roofline": pre["roofline"],
         "attention_ms": pre["attention_ms"],
+        "quantize_kv_ms": pre["quantize_kv_ms"],
     }
     if "prefill_d256" in args.leg_list:
         line["prefill_d256"] = bench_prefill(args, 3, counter_key="prefill_d256")[0]
