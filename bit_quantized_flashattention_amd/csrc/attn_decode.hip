@@ -79,9 +79,78 @@ __device__ __forceinline__ void load_tile(TileOps<D>& t, const uint8_t* kc, cons
   }
 }
 
-// PH: the P-hat rule, as in the prefill kernel (0 = per 32-key block from the FP16 probabilities,
-// 1 = per tile, 2 = Direct-P codes)
+// One tile of the split kernel: scores, masking, row step, P-hat, P-hat [V-hat | 1] and the FP16
+// state update (o, l, m of the lane's query)
 template <int D, int MODE, int PH>
+__device__ __forceinline__ void decode_tile(const TileOps<D>& t_ops, int tile, int bc, int g, int64_t lk, int64_t shift,
+                                            bool live_col, const uint4* qreg, const uint32_t* qsc, h2 (*o)[2],
+                                            _Float16& l, float& m) {
+  constexpr int KSTEPS = TileOps<D>::KSTEPS;
+  constexpr int CB = TileOps<D>::CB;
+  constexpr float C = SoftmaxC<D>::value;
+  const int64_t k0 = (int64_t)tile * bc;
+  float s[32];
+#pragma unroll
+  for (int tt = 0; tt < 8; tt++) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < KSTEPS; st++) {
+      const uint32_t kw = tt < 4 ? t_ops.ksc[st].x : t_ops.ksc[st].y;
+      switch (tt & 3) {
+        case 0: acc = mfma_fp4_sel<0, 0>(t_ops.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+        case 1: acc = mfma_fp4_sel<1, 0>(t_ops.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+        case 2: acc = mfma_fp4_sel<2, 0>(t_ops.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+        default: acc = mfma_fp4_sel<3, 0>(t_ops.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) s[4 * tt + i] = acc[i];
+  }
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 32; k++) {
+    const int64_t key = k0 + 32 * g + s_key(k);
+    const bool vis = (32 * g + k < bc) && key < lk && key <= shift && live_col;
+    s[k] = vis ? s[k] : -INFINITY;
+    bmax = fmaxf(bmax, s[k]);
+  }
+  const float rmax = group_max4(bmax);
+  // integer running max and FP16 rescale factor (all four lane groups hold the same row
+  // maximum, so they agree); the P-hat scale of the lane's own 32-key block
+  const RowStep rs = row_step(rmax, m, C);
+  const PhatScale ps = phat_scale<PH == 2>(PH == 1 ? rmax : bmax, C, rs.mm);
+  uint32_t p16[16];
+  uint4 ph;
+  if constexpr (PH == 2) ph = phat_codes_direct(s, C, ps.neg_big_m);
+  else ph = phat_codes(s, C, ps.neg_big_m, p16);
+  const uint32_t psc = (uint32_t)(int)(ps.e + 127.0f);
+  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+  v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
+  float lsum = lacc[0];
+  if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16) * e8m0_as_float((int)ps.e));
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t vw = t_ops.vsc[cb / 4];
+    switch (cb & 3) {
+      case 0: pv = mfma_fp4_sel<0, 0>(t_ops.v[cb], vw, ph, psc, pv); break;
+      case 1: pv = mfma_fp4_sel<1, 0>(t_ops.v[cb], vw, ph, psc, pv); break;
+      case 2: pv = mfma_fp4_sel<2, 0>(t_ops.v[cb], vw, ph, psc, pv); break;
+      default: pv = mfma_fp4_sel<3, 0>(t_ops.v[cb], vw, ph, psc, pv); break;
+    }
+    state_update(o[cb], rs.alpha, pv);
+  }
+  l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
+  m = rs.m_new;
+}
+
+// PH: the P-hat rule, as in the prefill kernel (0 = per 32-key block from the FP16 probabilities,
+// 1 = per tile, 2 = Direct-P codes).  R: register sets of tile operands, so R - 1 tiles are in
+// flight while one is computed: 2 when the grid fills the SIMDs with waves (registers allow two
+// waves per SIMD), 4 when it leaves them at one wave or fewer (small batches), where the bytes
+// in flight per wave set the rate.
+template <int D, int MODE, int PH, int R>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   constexpr int KSTEPS = D >= 128 ? D / 128 : 1;
   constexpr int CB = D / 16;
@@ -108,9 +177,11 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   const uint8_t* ks = a.k_scales + ((int64_t)b * a.heads_kv + kvh) * rows32 * (D / kBlock);
   const uint8_t* vc = a.v_codes + ((int64_t)b * a.heads_kv + kvh) * D * (rows32 / 2);
   const uint8_t* vs = a.v_scales + ((int64_t)b * a.heads_kv + kvh) * D * (rows32 / kBlock);
-  // the first tile is put in flight before the query is loaded, so the two latencies overlap
-  TileOps<D> cur, nxt;
-  if (t_lo < t_hi) load_tile<D>(cur, kc, ks, vc, vs, (int64_t)t_lo * bc, lk, lk32, rows32, bc, col, g);
+  // the first R - 1 tiles are put in flight before the query is loaded, so the latencies overlap
+  TileOps<D> buf[R];
+#pragma unroll
+  for (int u = 0; u < R - 1; u++)
+    if (t_lo + u < t_hi) load_tile<D>(buf[u], kc, ks, vc, vs, (int64_t)(t_lo + u) * bc, lk, lk32, rows32, bc, col, g);
 
   // Q-hat^T operand: column = query head, K-chunk g
   uint4 qreg[KSTEPS];
@@ -154,64 +225,84 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(AttnArgs a) {
   _Float16 l = (_Float16)0.0f;
   float m = -INFINITY;
 
-  for (int tile = t_lo; tile < t_hi; tile++) {
-    const int64_t k0 = (int64_t)tile * bc;
-    if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, k0 + bc, lk, lk32, rows32, bc, col, g);
-    float s[32];
+  if constexpr (R == 2) {
+    // one tile ahead: the next tile loads into nxt, which then becomes cur.  The tile body is
+    // decode_tile's, written out here: through the function this loop ran 2 % slower (register
+    // allocation), while the ring below gains from it
+    TileOps<D>& cur = buf[0];
+    TileOps<D>& nxt = buf[1];
+    for (int tile = t_lo; tile < t_hi; tile++) {
+      if (tile + 1 < t_hi) load_tile<D>(nxt, kc, ks, vc, vs, (int64_t)(tile + 1) * bc, lk, lk32, rows32, bc, col, g);
+      const int64_t k0 = (int64_t)tile * bc;
+      float s[32];
 #pragma unroll
-    for (int tt = 0; tt < 8; tt++) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tt = 0; tt < 8; tt++) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int st = 0; st < KSTEPS; st++) {
-        const uint32_t kw = tt < 4 ? cur.ksc[st].x : cur.ksc[st].y;
-        switch (tt & 3) {
-          case 0: acc = mfma_fp4_sel<0, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
-          case 1: acc = mfma_fp4_sel<1, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
-          case 2: acc = mfma_fp4_sel<2, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
-          default: acc = mfma_fp4_sel<3, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+        for (int st = 0; st < KSTEPS; st++) {
+          const uint32_t kw = tt < 4 ? cur.ksc[st].x : cur.ksc[st].y;
+          switch (tt & 3) {
+            case 0: acc = mfma_fp4_sel<0, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+            case 1: acc = mfma_fp4_sel<1, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+            case 2: acc = mfma_fp4_sel<2, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+            default: acc = mfma_fp4_sel<3, 0>(cur.k[tt][st], kw, qreg[st], qsc[st], acc); break;
+          }
         }
+#pragma unroll
+        for (int i = 0; i < 4; i++) s[4 * tt + i] = acc[i];
       }
+      float bmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; i++) s[4 * tt + i] = acc[i];
-    }
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 32; k++) {
-      const int64_t key = k0 + 32 * g + s_key(k);
-      const bool vis = (32 * g + k < bc) && key < lk && key <= shift && live_col;
-      s[k] = vis ? s[k] : -INFINITY;
-      bmax = fmaxf(bmax, s[k]);
-    }
-    const float rmax = group_max4(bmax);
-    // integer running max and FP16 rescale factor (all four lane groups hold the same row
-    // maximum, so they agree); the P-hat scale of the lane's own 32-key block
-    const RowStep rs = row_step(rmax, m, C);
-    const PhatScale ps = phat_scale<PH == 2>(PH == 1 ? rmax : bmax, C, rs.mm);
-    uint32_t p16[16];
-    uint4 ph;
-    if constexpr (PH == 2) ph = phat_codes_direct(s, C, ps.neg_big_m);
-    else ph = phat_codes(s, C, ps.neg_big_m, p16);
-    const uint32_t psc = (uint32_t)(int)(ps.e + 127.0f);
-    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
-    v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
-    lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
-    float lsum = lacc[0];
-    if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16) * e8m0_as_float((int)ps.e));
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-      v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
-      const uint32_t vw = cur.vsc[cb / 4];
-      switch (cb & 3) {
-        case 0: pv = mfma_fp4_sel<0, 0>(cur.v[cb], vw, ph, psc, pv); break;
-        case 1: pv = mfma_fp4_sel<1, 0>(cur.v[cb], vw, ph, psc, pv); break;
-        case 2: pv = mfma_fp4_sel<2, 0>(cur.v[cb], vw, ph, psc, pv); break;
-        default: pv = mfma_fp4_sel<3, 0>(cur.v[cb], vw, ph, psc, pv); break;
+      for (int k = 0; k < 32; k++) {
+        const int64_t key = k0 + 32 * g + s_key(k);
+        const bool vis = (32 * g + k < bc) && key < lk && key <= shift && live_col;
+        s[k] = vis ? s[k] : -INFINITY;
+        bmax = fmaxf(bmax, s[k]);
       }
-      state_update(o[cb], rs.alpha, pv);
+      const float rmax = group_max4(bmax);
+      // integer running max and FP16 rescale factor (all four lane groups hold the same row
+      // maximum, so they agree); the P-hat scale of the lane's own 32-key block
+      const RowStep rs = row_step(rmax, m, C);
+      const PhatScale ps = phat_scale<PH == 2>(PH == 1 ? rmax : bmax, C, rs.mm);
+      uint32_t p16[16];
+      uint4 ph;
+      if constexpr (PH == 2) ph = phat_codes_direct(s, C, ps.neg_big_m);
+      else ph = phat_codes(s, C, ps.neg_big_m, p16);
+      const uint32_t psc = (uint32_t)(int)(ps.e + 127.0f);
+      const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+      v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+      lacc = mfma_fp4(ones, 127u, ph, psc, lacc);
+      float lsum = lacc[0];
+      if (MODE == 1) lsum = group_sum4(tree_sum32_h(p16) * e8m0_as_float((int)ps.e));
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) {
+        v4f pv = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t vw = cur.vsc[cb / 4];
+        switch (cb & 3) {
+          case 0: pv = mfma_fp4_sel<0, 0>(cur.v[cb], vw, ph, psc, pv); break;
+          case 1: pv = mfma_fp4_sel<1, 0>(cur.v[cb], vw, ph, psc, pv); break;
+          case 2: pv = mfma_fp4_sel<2, 0>(cur.v[cb], vw, ph, psc, pv); break;
+          default: pv = mfma_fp4_sel<3, 0>(cur.v[cb], vw, ph, psc, pv); break;
+        }
+        state_update(o[cb], rs.alpha, pv);
+      }
+      l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
+      m = rs.m_new;
+      if (tile + 1 < t_hi) cur = nxt;
     }
-    l = __builtin_fmaf16(rs.alpha, l, (_Float16)lsum);
-    m = rs.m_new;
-    if (tile + 1 < t_hi) cur = nxt;
+  } else {
+    // ring of R operand sets: tile t uses set (t - t_lo) % R; before computing it, tile t + R - 1
+    // is put in flight into the set tile t - 1 used
+    for (int base = t_lo; base < t_hi; base += R) {
+#pragma unroll
+      for (int u = 0; u < R; u++) {
+        const int tile = base + u;
+        if (tile >= t_hi) break;
+        if (tile + R - 1 < t_hi)
+          load_tile<D>(buf[(u + R - 1) % R], kc, ks, vc, vs, (int64_t)(tile + R - 1) * bc, lk, lk32, rows32, bc, col, g);
+        decode_tile<D, MODE, PH>(buf[u], tile, bc, g, lk, shift, live_col, qreg, qsc, o, l, m);
+      }
+    }
   }
 
   if (!live_col) return;
@@ -253,15 +344,39 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
   a.out[bh * D + ch] = __builtin_bit_cast(uint16_t, (_Float16)(o / l));
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static int cus[kDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+template <int D, int R>
+void launch_split(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1, 0, R>), grid, dim3(64), 0, s, a);
+  else if (a.phat == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 1, R>), grid, dim3(64), 0, s, a);
+  else if (a.phat == 2) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 2, R>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 0, R>), grid, dim3(64), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   if (a.c_log2 != SoftmaxC<D>::value) return hipErrorInvalidValue;  // the kernel's constant must be the caller's C
   const int group = a.heads_q / a.heads_kv;
   dim3 grid((uint32_t)a.num_splits, (uint32_t)(a.heads_kv * ((group + 15) / 16)), (uint32_t)a.batch);
-  if (a.normalizer == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 1, 0>), grid, dim3(64), 0, s, a);
-  else if (a.phat == 1) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 1>), grid, dim3(64), 0, s, a);
-  else if (a.phat == 2) hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 2>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((attn_decode_split_kernel<D, 0, 0>), grid, dim3(64), 0, s, a);
+  // one wave per work-group: with no more waves than SIMDs, each wave keeps three tiles in flight
+  // (d <= 128; d = 256 operand sets do not fit four times in the registers)
+  const int64_t waves = (int64_t)grid.x * grid.y * grid.z;
+  if (D <= 128 && waves <= 4 * (int64_t)device_cus()) launch_split<D, D <= 128 ? 4 : 2>(a, grid, s);
+  else launch_split<D, 2>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((uint32_t)((int64_t)a.batch * a.heads_q)), dim3(D), 0, s, a);
