@@ -93,6 +93,18 @@ def test_decode_split_kv(d, splits, normalizer):
     compare_out(got, want, "decode-d%d-s%d" % (d, splits))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_grid_beyond_one_wave_per_simd(d):
+    """16 x 8 (batch, KV head) units x 12 splits = 1536 single-wave work-groups, more than the
+    1024 SIMDs of the chip: the split kernel then keeps one tile in flight (two operand sets)
+    instead of three, the small-grid choice the other decode cases take.  17 tiles of 128 keys
+    (the last ragged) over 12 splits of 2 leave three splits empty."""
+    cfg, q, k, v, cal = gen(1, B=16, Hq=8, Hkv=8, Lq=1, Lk=2100, d=d)
+    print("case decode large grid d", d, flush=True)
+    got, want, *_ = run_case(q, k, v, True, 128, calib=cal, num_splits=12)
+    compare_out(got, want, "decode-grid-d%d" % d)
+
+
 def test_decode_workspace_reuse_and_head_chunks():
     """GQA group of 32 (two 16-head chunks per KV head, two split waves per (batch, KV head,
     split)); repeated calls on one workspace give identical outputs."""
