@@ -272,14 +272,14 @@ hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, cons
   const int group = dims->heads_q / dims->heads_kv;
   if (q) {
     hifa4::QuantRopeArgs a{(const uint16_t*)q, s, rope_cos, rope_sin, dims->batch, dims->len_q, round32(dims->len_q),
-                           dims->len_kv - dims->len_q, dims->heads_q, group, dims->heads_kv, dims->head_dim, 0, 0,
+                           dims->len_kv - dims->len_q, dims->heads_q, group, dims->heads_kv, dims->head_dim, 0,
                            (uint8_t*)q_codes, (uint8_t*)q_scales};
     hipError_t e = hifa4::launch_quantize_rope(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
   }
   if (k) {
     hifa4::QuantRopeArgs a{(const uint16_t*)k, inv_s, rope_cos, rope_sin, dims->batch, dims->len_kv,
-                           round32(dims->len_kv), 0, dims->heads_kv, 1, dims->heads_kv, dims->head_dim, 1, 0,
+                           round32(dims->len_kv), 0, dims->heads_kv, 1, dims->heads_kv, dims->head_dim, 1,
                            (uint8_t*)k_codes, (uint8_t*)k_scales};
     hipError_t e = hifa4::launch_quantize_rope(a, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));

@@ -77,7 +77,6 @@ struct QuantRopeArgs {
   int32_t scale_rows;   // Hs (rows of scale)
   int32_t d;
   int32_t block_planes; // 0: scales [rows, d/32] (Q-hat); 1: [B*H, d/32, len32] (K-hat), tail 0
-  int32_t pos_per_wg;   // positions per work-group (set by the launcher)
   uint8_t* codes;       // [B*H*len, d/2]
   uint8_t* scales;
 };

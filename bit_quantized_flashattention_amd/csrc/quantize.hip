@@ -140,102 +140,129 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(QuantRowsArgs ka, Quan
   }
 }
 
-// RoPE (FP32, rotate-half), Smooth-QK and 4-bit quantization of pre-RoPE rows, fused.  A
-// work-group serves kRopeMaxPos consecutive positions of one batch entry for all H heads, so the
-// cos/sin rows of those positions (and the Smooth-QK scale table when it is small) are staged in
-// LDS once and shared by every head.  An item is one (position, head, block pair j): channels
-// 32 j .. 32 j + 31 and their rotation partners 32 j + d/2 .. , so each item writes two
-// quantization blocks.  Rounding, as the rotation is defined for this prologue: each product
-// and each sum once in FP32, no fused multiply-add (contraction is off), then fp32(y * s).
-constexpr int kRopeMaxPos = 32;          // positions per work-group at most
-constexpr int kRopeMaxScaleFloats = 4096;  // Smooth-QK tables up to 16 KB are staged in LDS
+// RoPE (FP32, rotate-half), Smooth-QK and 4-bit quantization of pre-RoPE rows, fused.  An item
+// is one (position, block pair j): channels 32 j .. 32 j + 31 of a row and their rotation
+// partners 32 j + d/2 .., so each item writes two quantization blocks.  Four adjacent lanes
+// share an item: lane q rotates channels 8 q .. 8 q + 7 of both blocks, the two block maxima are
+// reduced over the four lanes, and each lane packs its 8 + 8 codes (4 bytes of each block's 16).
+// A work-group takes kRopeItems groups of 64 items (64 / (d/64) consecutive positions each) of
+// one (batch, head), so consecutive work-groups read consecutive rows and the grid sweeps HBM in
+// order; the cos/sin rows come from the (L2-resident) tables, the head's Smooth-QK row is staged
+// in LDS.  Rounding, as the rotation is defined for this prologue: each product and each sum
+// once in FP32, no fused multiply-add (contraction is off), then fp32(y * s).
+constexpr int kRopeItems = 2;  // items per quad: consecutive position groups of one work-group
+
+template <int D>
+constexpr int rope_positions() { return kRopeItems * 64 / (D / 64); }
+
+// Largest of v over the four lanes of an aligned quad (all four lanes active).
+__device__ __forceinline__ float quad_max(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));  // lanes 1 0 3 2
+  const int c = __builtin_bit_cast(int, v);
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(c, c, 0x4E, 0xF, 0xF, false)));  // 2 3 0 1
+}
+
+// The 8 FP16 values of one 16-byte load as FP32 (exact).
+__device__ __forceinline__ void unpack8(const uint4& w, float* v) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x[i] & 0xFFFF));
+    v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x[i] >> 16));
+  }
+}
 
 template <int D, bool PLANES>
 __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
   constexpr int NB = D / kBlock;
   constexpr int NP = NB / 2;  // block pairs per row
   constexpr int H2 = D / 2;
-  __shared__ __attribute__((aligned(16))) float s_cos[kRopeMaxPos * H2];
-  __shared__ __attribute__((aligned(16))) float s_sin[kRopeMaxPos * H2];
-  __shared__ __attribute__((aligned(16))) float s_scale[kRopeMaxScaleFloats];
-  const int P = a.pos_per_wg;
-  const int64_t b = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * P;  // first token of the work-group
-  const int64_t n_tok = PLANES ? a.len32 : a.len;
-  const int np = (int)(n_tok - t0 < P ? n_tok - t0 : P);
-  const int nrot = (int)(a.len - t0 < np ? (a.len - t0 > 0 ? a.len - t0 : 0) : np);  // tokens with data
-  for (int i = threadIdx.x; i < nrot * H2; i += blockDim.x) {
-    const int64_t src = (a.pos0 + t0 + i / H2) * H2 + i % H2;
-    s_cos[i] = a.rope_cos[src];
-    s_sin[i] = a.rope_sin[src];
+  constexpr int U = kRopeItems;
+  constexpr int PU = 64 / NP;  // positions per item group (64 items, one per quad)
+  __shared__ __attribute__((aligned(16))) float s_scale[D];
+  const int h = blockIdx.y;
+  const int64_t bh = (int64_t)blockIdx.z * a.heads + h;
+  const int j = (threadIdx.x >> 2) % NP;
+  const int q = threadIdx.x & 3;
+  const int c = kBlock * j + 8 * q;  // the lane's first channel in the low block
+  const bool scaled = a.scale != nullptr;
+  // the loads go out in this order: the Smooth-QK row (one value per thread, D <= 256), then the
+  // items' rows and table entries, as straight-line code (the compiler counts loads in flight
+  // only outside branches); the LDS write waits for the first only, so the barrier and the
+  // items' loads overlap in one memory round trip.  Unscaled calls read an unused table entry
+  // instead, and tokens past the data read row len - 1 without using it.
+  const float sv = scaled ? a.scale[(int64_t)(h / a.heads_per_scale_row) * D + (threadIdx.x & (D - 1))]
+                          : a.rope_cos[threadIdx.x & (H2 - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keeps that load ahead of the items' loads
+  int64_t tok[U];
+  uint4 xl[U], xh[U];
+  float4 c0[U], c1[U], s0[U], s1[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    tok[u] = ((int64_t)blockIdx.x * U + u) * PU + (threadIdx.x >> 2) / NP;
+    const int64_t tc = tok[u] < a.len ? tok[u] : a.len - 1;
+    const uint16_t* x = a.x + (bh * a.len + tc) * D;
+    xl[u] = *reinterpret_cast<const uint4*>(x + c);
+    xh[u] = *reinterpret_cast<const uint4*>(x + H2 + c);
+    const float4* cp = reinterpret_cast<const float4*>(a.rope_cos + (a.pos0 + tc) * H2 + c);
+    const float4* sp = reinterpret_cast<const float4*>(a.rope_sin + (a.pos0 + tc) * H2 + c);
+    c0[u] = cp[0];
+    c1[u] = cp[1];
+    s0[u] = sp[0];
+    s1[u] = sp[1];
   }
-  const bool staged = a.scale != nullptr && a.scale_rows * D <= kRopeMaxScaleFloats;
-  if (staged)
-    for (int i = threadIdx.x; i < a.scale_rows * D; i += blockDim.x) s_scale[i] = a.scale[i];
+  if (threadIdx.x < D) s_scale[threadIdx.x] = sv;
   __syncthreads();
-  // items ordered (head, position, block pair): the threads of a wave read consecutive rows of
-  // one head, i.e. one contiguous run of HBM
-  const int items = P * a.heads * NP;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int j = it % NP;
-    const int pl = (it / NP) % P;
-    const int h = it / (NP * P);
-    if (pl >= np) continue;
-    const int64_t tok = t0 + pl;
-    const int64_t bh = b * a.heads + h;
-    if (tok >= a.len) {  // padding key of a scale plane: zero scale bytes for both blocks
-      if (PLANES) {
-        a.scales[(bh * NB + j) * a.len32 + tok] = 0;
-        a.scales[(bh * NB + j + NP) * a.len32 + tok] = 0;
-      }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    if (tok[u] >= (PLANES ? a.len32 : a.len)) break;  // later groups lie further out
+    if (tok[u] >= a.len) {  // padding key of a scale plane: zero scale bytes for both blocks
+      if (PLANES && q < 2) a.scales[(bh * NB + j + q * NP) * a.len32 + tok[u]] = 0;
       continue;
     }
-    const int64_t row = bh * a.len + tok;
-    Block32In lo_in, hi_in;
-    load_block32(a.x + row * D + kBlock * j, nullptr, lo_in);
-    load_block32(a.x + row * D + H2 + kBlock * j, nullptr, hi_in);
-    float lo[32], hi[32];
-    unpack_block32(lo_in, lo);
-    unpack_block32(hi_in, hi);
-    const float* cs = s_cos + pl * H2 + kBlock * j;
-    const float* sn = s_sin + pl * H2 + kBlock * j;
+    const int64_t row = bh * a.len + tok[u];
+    const float cs[8] = {c0[u].x, c0[u].y, c0[u].z, c0[u].w, c1[u].x, c1[u].y, c1[u].z, c1[u].w};
+    const float sn[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+    float lo[8], hi[8];
+    unpack8(xl[u], lo);
+    unpack8(xh[u], hi);
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
+    for (int i = 0; i < 8; i++) {
       const float x0 = lo[i], x1 = hi[i];
-      const float c = cs[i], s = sn[i];
-      lo[i] = x0 * c - x1 * s;  // RN32 of each product, then of the difference
-      hi[i] = x1 * c + x0 * s;
+      lo[i] = x0 * cs[i] - x1 * sn[i];  // RN32 of each product, then of the difference
+      hi[i] = x1 * cs[i] + x0 * sn[i];
     }
-    if (a.scale != nullptr) {
-      const int srow = h / a.heads_per_scale_row;
-      const float* sc = staged ? s_scale + srow * D : a.scale + (int64_t)srow * D;
+    if (scaled) {
 #pragma unroll
-      for (int i = 0; i < 32; i++) {
-        lo[i] = lo[i] * sc[kBlock * j + i];
-        hi[i] = hi[i] * sc[H2 + kBlock * j + i];
+      for (int i = 0; i < 8; i++) {
+        lo[i] = lo[i] * s_scale[c + i];
+        hi[i] = hi[i] * s_scale[H2 + c + i];
       }
     }
-    uint4 c_lo, c_hi;
-    const uint32_t e_lo = quantize_values32(lo, &c_lo);
-    const uint32_t e_hi = quantize_values32(hi, &c_hi);
-    *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + 16 * j) = c_lo;
-    *reinterpret_cast<uint4*>(a.codes + row * (D / 2) + 16 * (j + NP)) = c_hi;
-    if (PLANES) {
-      a.scales[(bh * NB + j) * a.len32 + tok] = (uint8_t)e_lo;
-      a.scales[(bh * NB + j + NP) * a.len32 + tok] = (uint8_t)e_hi;
-    } else {
-      a.scales[row * NB + j] = (uint8_t)e_lo;
-      a.scales[row * NB + j + NP] = (uint8_t)e_hi;
+    float ml = 0.0f, mh = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      ml = fmaxf(ml, fabsf(lo[i]));
+      mh = fmaxf(mh, fabsf(hi[i]));
+    }
+    const int e_lo = mx_exponent(quad_max(ml)), e_hi = mx_exponent(quad_max(mh));
+    uint8_t* crow = a.codes + row * (D / 2);
+    *reinterpret_cast<uint32_t*>(crow + 16 * j + 4 * q) = pack8_fp4(lo, e8m0_as_float(e_lo));
+    *reinterpret_cast<uint32_t*>(crow + 16 * (j + NP) + 4 * q) = pack8_fp4(hi, e8m0_as_float(e_hi));
+    if (q < 2) {
+      const uint8_t e8 = (uint8_t)((q == 0 ? e_lo : e_hi) + 127);
+      if (PLANES) a.scales[(bh * NB + j + q * NP) * a.len32 + tok[u]] = e8;
+      else a.scales[row * NB + j + q * NP] = e8;
     }
   }
 }
 
 template <int D>
 static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
-  const int p = kRopeMaxPos;
-  a.pos_per_wg = p;
+  constexpr int p = rope_positions<D>();
   const int64_t n_tok = a.block_planes ? a.len32 : a.len;
-  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)a.batch);
+  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)a.heads, (uint32_t)a.batch);
   if (a.block_planes) hipLaunchKernelGGL((quantize_rope_kernel<D, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((quantize_rope_kernel<D, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
