@@ -18,17 +18,20 @@ from gpu_helpers import NAMES, assert_codes_equal, compare_out, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _case(cfg_id, causal, kv_tile, **over):
+def _case(cfg_id, causal, kv_tile, smooth_qk=True, **over):
     import torch
     cfg = synth.config(cfg_id, **over)
     theta = cfg["rope_theta"] or 1e4
     q, k, v = synth.make_qkv(cfg, pre_rope=True)
     qc, kc = synth.make_calibration(cfg)
     s32, inv32, gate = smooth.calibrate(qc, kc, cfg["alpha"], 4.0)
+    if not smooth_qk:
+        s32 = inv32 = None
     cos32, sin32 = synth.rope_table(theta, cfg["Lk"], cfg["d"])
-    print("case rope", cfg_id, over, flush=True)
-    res = hf.quantize_qkv_rope(to_dev(q), to_dev(k), to_dev(v), to_dev(s32), to_dev(inv32), to_dev(cos32),
-                               to_dev(sin32))
+    print("case rope", cfg_id, over, "smooth" if smooth_qk else "no smooth", flush=True)
+    sd = to_dev(s32) if s32 is not None else None
+    invd = to_dev(inv32) if inv32 is not None else None
+    res = hf.quantize_qkv_rope(to_dev(q), to_dev(k), to_dev(v), sd, invd, to_dev(cos32), to_dev(sin32))
     qq = rope.quantize_qkv_rope(q, k, v, s32, inv32, cos32, sin32)
     assert_codes_equal(res, qq)
     dims = hf.make_dims(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lq"], cfg["Lk"])
@@ -40,7 +43,7 @@ def _case(cfg_id, causal, kv_tile, **over):
     # decode: the fused-Q entry point rotates the pre-RoPE query in its prologue, bit-identically;
     # prefill refuses the tables (the streaming RoPE quantizer is the faster route there)
     kv_only = {n: res[n] for n in NAMES[2:]}
-    q16 = (to_dev(q), to_dev(s32), to_dev(cos32), to_dev(sin32))
+    q16 = (to_dev(q), sd, to_dev(cos32), to_dev(sin32))
     if cfg["Lq"] == 1:
         out16 = hf.attention_fwd(kv_only, dims, causal, 0, kv_tile, q16=q16)
         torch.cuda.synchronize()
@@ -75,10 +78,18 @@ def test_rope_decode_d64_and_d256():
     _case(3, True, 128, B=2, Hq=8, Hkv=2, Lq=1, Lk=300)
 
 
-def test_rope_wide_group_two_items_per_thread():
-    # 64 query heads per KV head at d = 256: 512 items per position, one position per
-    # work-group, so each thread serves two items
+def test_rope_wide_group_d256():
+    # 64 query heads share each Smooth-QK row at d = 256; 24 positions, fewer than one
+    # work-group's 32
     _case(3, False, 128, B=1, Hq=128, Hkv=2, Lq=24, Lk=24)
+
+
+def test_rope_without_smooth_qk_one_past_a_work_group():
+    # no Smooth-QK tables (rotation and quantization only); 129 positions at d = 128: a
+    # work-group takes 128, so the second one has a single live row and pads K's scale planes
+    # to 160
+    _case(1, True, 128, smooth_qk=False, B=2, Hq=8, Hkv=2, Lq=129, Lk=129)
+    _case(0, False, 64, smooth_qk=False, B=1, Hq=2, Hkv=2, Lq=257, Lk=257)
 
 
 def test_rope_full_size_batched_prefill():
