@@ -2,7 +2,8 @@
 //
 // Decode is HBM-bound: every K-hat/V-hat byte is used by exactly one MFMA lane once, so the
 // kernel skips LDS and loads each lane's MFMA operands straight from HBM into registers, one
-// tile ahead of the computation.  The query heads of a GQA group are the MFMA columns (the
+// tile ahead of the computation (three when the grid leaves a SIMD at most one wave, where the
+// bytes in flight per wave set the rate).  The query heads of a GQA group are the MFMA columns (the
 // same S^T = K-hat Q-hat^T layout as the prefill kernel, see attn_prefill.hip), so a wave
 // serves one (batch, KV head, split) and keeps its split's FP16 state in registers.
 #include <mutex>
