@@ -145,15 +145,16 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(QuantRowsArgs ka, Quan
 // partners 32 j + d/2 .., so each item writes two quantization blocks.  Four adjacent lanes
 // share an item: lane q rotates channels 8 q .. 8 q + 7 of both blocks, the two block maxima are
 // reduced over the four lanes, and each lane packs its 8 + 8 codes (4 bytes of each block's 16).
-// A work-group takes kRopeItems groups of 64 items (64 / (d/64) consecutive positions each) of
-// one (batch, head), so consecutive work-groups read consecutive rows and the grid sweeps HBM in
-// order; the cos/sin rows come from the (L2-resident) tables, the head's Smooth-QK row is staged
-// in LDS.  Rounding, as the rotation is defined for this prologue: each product and each sum
-// once in FP32, no fused multiply-add (contraction is off), then fp32(y * s).
-constexpr int kRopeItems = 2;  // items per quad: consecutive position groups of one work-group
+// A work-group takes 64 items (64 / (d/64) consecutive positions) of kRopeHeads heads of one
+// batch entry: a lane reads its cos/sin entries once from the (L2-resident) tables and applies
+// them to the same item of each head, and consecutive work-groups read consecutive rows of each
+// head.  The heads' Smooth-QK rows are staged in LDS.  Rounding, as the rotation is defined for
+// this prologue: each product and each sum once in FP32, no fused multiply-add (contraction is
+// off), then fp32(y * s).
+constexpr int kRopeHeads = 4;  // heads per work-group sharing each lane's cos/sin registers
 
 template <int D>
-constexpr int rope_positions() { return kRopeItems * 64 / (D / 64); }
+constexpr int rope_positions() { return 64 / (D / 64); }
 
 // Largest of v over the four lanes of an aligned quad (all four lanes active).
 __device__ __forceinline__ float quad_max(float v) {
@@ -178,55 +179,62 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
   constexpr int NB = D / kBlock;
   constexpr int NP = NB / 2;  // block pairs per row
   constexpr int H2 = D / 2;
-  constexpr int U = kRopeItems;
-  constexpr int PU = 64 / NP;  // positions per item group (64 items, one per quad)
-  __shared__ __attribute__((aligned(16))) float s_scale[D];
-  const int h = blockIdx.y;
-  const int64_t bh = (int64_t)blockIdx.z * a.heads + h;
+  constexpr int G = kRopeHeads;
+  constexpr int P = rope_positions<D>();  // P * NP = 64 items, one per quad
+  constexpr int SV = (G * D + 255) / 256;  // staged Smooth-QK values per thread
+  __shared__ __attribute__((aligned(16))) float s_scale[G * D];
+  const int h0 = blockIdx.y * G;
+  const int64_t b = blockIdx.z;
+  const int64_t tok = (int64_t)blockIdx.x * P + (threadIdx.x >> 2) / NP;
   const int j = (threadIdx.x >> 2) % NP;
   const int q = threadIdx.x & 3;
   const int c = kBlock * j + 8 * q;  // the lane's first channel in the low block
   const bool scaled = a.scale != nullptr;
-  // the loads go out in this order: the Smooth-QK row (one value per thread, D <= 256), then the
-  // items' rows and table entries, as straight-line code (the compiler counts loads in flight
-  // only outside branches); the LDS write waits for the first only, so the barrier and the
-  // items' loads overlap in one memory round trip.  Unscaled calls read an unused table entry
-  // instead, and tokens past the data read row len - 1 without using it.
-  const float sv = scaled ? a.scale[(int64_t)(h / a.heads_per_scale_row) * D + (threadIdx.x & (D - 1))]
-                          : a.rope_cos[threadIdx.x & (H2 - 1)];
-  __builtin_amdgcn_sched_barrier(0);  // keeps that load ahead of the items' loads
-  int64_t tok[U];
-  uint4 xl[U], xh[U];
-  float4 c0[U], c1[U], s0[U], s1[U];
+  // the loads go out in this order: the heads' Smooth-QK rows, then the table entries and the
+  // rows, as straight-line code (the compiler counts loads in flight only outside branches); the
+  // LDS writes wait for the first loads only, so the barrier and the rows' loads overlap in one
+  // memory round trip.  Unscaled calls read unused table entries instead, heads past H and
+  // tokens past the data read head H - 1 and row len - 1 without using them.
+  float sv[SV];
 #pragma unroll
-  for (int u = 0; u < U; u++) {
-    tok[u] = ((int64_t)blockIdx.x * U + u) * PU + (threadIdx.x >> 2) / NP;
-    const int64_t tc = tok[u] < a.len ? tok[u] : a.len - 1;
-    const uint16_t* x = a.x + (bh * a.len + tc) * D;
-    xl[u] = *reinterpret_cast<const uint4*>(x + c);
-    xh[u] = *reinterpret_cast<const uint4*>(x + H2 + c);
-    const float4* cp = reinterpret_cast<const float4*>(a.rope_cos + (a.pos0 + tc) * H2 + c);
-    const float4* sp = reinterpret_cast<const float4*>(a.rope_sin + (a.pos0 + tc) * H2 + c);
-    c0[u] = cp[0];
-    c1[u] = cp[1];
-    s0[u] = sp[0];
-    s1[u] = sp[1];
+  for (int i = 0; i < SV; i++) {
+    const int e = i * 256 + threadIdx.x;  // (head g, channel) = (e / D, e % D)
+    const int hs = min(h0 + (e / D) % G, a.heads - 1);
+    sv[i] = scaled ? a.scale[(int64_t)(hs / a.heads_per_scale_row) * D + e % D] : a.rope_cos[e % H2];
   }
-  if (threadIdx.x < D) s_scale[threadIdx.x] = sv;
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);  // keeps those loads ahead of the rows' loads
+  const bool live = tok < a.len;
+  const int64_t tc = live ? tok : a.len - 1;
+  const float4* cp = reinterpret_cast<const float4*>(a.rope_cos + (a.pos0 + tc) * H2 + c);
+  const float4* sp = reinterpret_cast<const float4*>(a.rope_sin + (a.pos0 + tc) * H2 + c);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  uint4 xl[G], xh[G];
 #pragma unroll
-  for (int u = 0; u < U; u++) {
-    if (tok[u] >= (PLANES ? a.len32 : a.len)) break;  // later groups lie further out
-    if (tok[u] >= a.len) {  // padding key of a scale plane: zero scale bytes for both blocks
-      if (PLANES && q < 2) a.scales[(bh * NB + j + q * NP) * a.len32 + tok[u]] = 0;
+  for (int g = 0; g < G; g++) {
+    const int hg = min(h0 + g, a.heads - 1);
+    const uint16_t* x = a.x + ((b * a.heads + hg) * a.len + tc) * D;
+    xl[g] = *reinterpret_cast<const uint4*>(x + c);
+    xh[g] = *reinterpret_cast<const uint4*>(x + H2 + c);
+  }
+#pragma unroll
+  for (int i = 0; i < SV; i++)
+    if (i * 256 + threadIdx.x < G * D) s_scale[i * 256 + threadIdx.x] = sv[i];
+  __syncthreads();
+  if (tok >= (PLANES ? a.len32 : a.len)) return;
+  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    if (h0 + g >= a.heads) break;
+    const int64_t bh = b * a.heads + h0 + g;
+    if (!live) {  // padding key of a scale plane: zero scale bytes for both blocks
+      if (PLANES && q < 2) a.scales[(bh * NB + j + q * NP) * a.len32 + tok] = 0;
       continue;
     }
-    const int64_t row = bh * a.len + tok[u];
-    const float cs[8] = {c0[u].x, c0[u].y, c0[u].z, c0[u].w, c1[u].x, c1[u].y, c1[u].z, c1[u].w};
-    const float sn[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+    const int64_t row = bh * a.len + tok;
     float lo[8], hi[8];
-    unpack8(xl[u], lo);
-    unpack8(xh[u], hi);
+    unpack8(xl[g], lo);
+    unpack8(xh[g], hi);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float x0 = lo[i], x1 = hi[i];
@@ -234,10 +242,11 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
       hi[i] = x1 * cs[i] + x0 * sn[i];
     }
     if (scaled) {
+      const float* sc = s_scale + g * D + c;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        lo[i] = lo[i] * s_scale[c + i];
-        hi[i] = hi[i] * s_scale[H2 + c + i];
+        lo[i] = lo[i] * sc[i];
+        hi[i] = hi[i] * sc[H2 + i];
       }
     }
     float ml = 0.0f, mh = 0.0f;
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
     *reinterpret_cast<uint32_t*>(crow + 16 * (j + NP) + 4 * q) = pack8_fp4(hi, e8m0_as_float(e_hi));
     if (q < 2) {
       const uint8_t e8 = (uint8_t)((q == 0 ? e_lo : e_hi) + 127);
-      if (PLANES) a.scales[(bh * NB + j + q * NP) * a.len32 + tok[u]] = e8;
+      if (PLANES) a.scales[(bh * NB + j + q * NP) * a.len32 + tok] = e8;
       else a.scales[row * NB + j + q * NP] = e8;
     }
   }
@@ -262,7 +271,7 @@ template <int D>
 static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
   constexpr int p = rope_positions<D>();
   const int64_t n_tok = a.block_planes ? a.len32 : a.len;
-  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)a.heads, (uint32_t)a.batch);
+  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)((a.heads + kRopeHeads - 1) / kRopeHeads), (uint32_t)a.batch);
   if (a.block_planes) hipLaunchKernelGGL((quantize_rope_kernel<D, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((quantize_rope_kernel<D, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
