@@ -270,24 +270,29 @@ hifa4_status hifa4_quantize_qkv_rope(const hifa4_dims* dims, const void* q, cons
     return fail(HIFA4_ERR_ALIGNMENT, "quantize: device pointers must be 16-byte aligned");
   hipStream_t stream = (hipStream_t)hip_stream;
   const int group = dims->heads_q / dims->heads_kv;
+  const hifa4::QuantRopeArgs qa{(const uint16_t*)q, s, rope_cos, rope_sin, dims->batch, dims->len_q,
+                                round32(dims->len_q), dims->len_kv - dims->len_q, dims->heads_q, group,
+                                dims->heads_kv, dims->head_dim, 0, (uint8_t*)q_codes, (uint8_t*)q_scales};
+  const hifa4::QuantRopeArgs ka{(const uint16_t*)k, inv_s, rope_cos, rope_sin, dims->batch, dims->len_kv,
+                                round32(dims->len_kv), 0, dims->heads_kv, 1, dims->heads_kv, dims->head_dim, 1,
+                                (uint8_t*)k_codes, (uint8_t*)k_scales};
+  const hifa4::QuantVtArgs va{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
+                              round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales};
+  if (q && k && v) {  // all three in one launch
+    hipError_t e = hifa4::launch_quantize_qkv_rope(qa, ka, va, stream);
+    if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q, k, v: ") + hipGetErrorString(e));
+    return ok();
+  }
   if (q) {
-    hifa4::QuantRopeArgs a{(const uint16_t*)q, s, rope_cos, rope_sin, dims->batch, dims->len_q, round32(dims->len_q),
-                           dims->len_kv - dims->len_q, dims->heads_q, group, dims->heads_kv, dims->head_dim, 0,
-                           (uint8_t*)q_codes, (uint8_t*)q_scales};
-    hipError_t e = hifa4::launch_quantize_rope(a, stream);
+    hipError_t e = hifa4::launch_quantize_rope(qa, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize q: ") + hipGetErrorString(e));
   }
   if (k) {
-    hifa4::QuantRopeArgs a{(const uint16_t*)k, inv_s, rope_cos, rope_sin, dims->batch, dims->len_kv,
-                           round32(dims->len_kv), 0, dims->heads_kv, 1, dims->heads_kv, dims->head_dim, 1,
-                           (uint8_t*)k_codes, (uint8_t*)k_scales};
-    hipError_t e = hifa4::launch_quantize_rope(a, stream);
+    hipError_t e = hifa4::launch_quantize_rope(ka, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize k: ") + hipGetErrorString(e));
   }
   if (v) {
-    hifa4::QuantVtArgs a{(const uint16_t*)v, (int64_t)dims->batch * dims->heads_kv, dims->len_kv,
-                         round32(dims->len_kv), dims->head_dim, (uint8_t*)v_codes, (uint8_t*)v_scales};
-    hipError_t e = hifa4::launch_quantize_vt(a, stream);
+    hipError_t e = hifa4::launch_quantize_vt(va, stream);
     if (e != hipSuccess) return fail(HIFA4_ERR_HIP, std::string("quantize v: ") + hipGetErrorString(e));
   }
   return ok();

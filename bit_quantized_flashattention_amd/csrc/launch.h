@@ -101,6 +101,9 @@ struct CacheAppendArgs {
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
 hipError_t launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
 hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s);
+// Q-hat (block_planes 0) and K-hat (block_planes 1) with RoPE and V-hat, one launch
+hipError_t launch_quantize_qkv_rope(const QuantRopeArgs& qa, const QuantRopeArgs& ka, const QuantVtArgs& va,
+                                    hipStream_t s);
 hipError_t launch_quantize_vt(const QuantVtArgs& a, hipStream_t s);
 // K-hat rows (block planes) and V-hat tiles of one (K, V) pair in one launch
 hipError_t launch_quantize_kv(const QuantRowsArgs& ka, const QuantVtArgs& va, hipStream_t s);

@@ -174,8 +174,10 @@ __device__ __forceinline__ void unpack8(const uint4& w, float* v) {
   }
 }
 
+// Work-group (bx, by, bz) of the RoPE quantizer's grid: position group bx, heads G by .. G by +
+// G - 1, batch entry bz.
 template <int D, bool PLANES>
-__global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
+__device__ __forceinline__ void quantize_rope_block(const QuantRopeArgs& a, int64_t bx, int by, int64_t bz) {
   constexpr int NB = D / kBlock;
   constexpr int NP = NB / 2;  // block pairs per row
   constexpr int H2 = D / 2;
@@ -183,9 +185,9 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
   constexpr int P = rope_positions<D>();  // P * NP = 64 items, one per quad
   constexpr int SV = (G * D + 255) / 256;  // staged Smooth-QK values per thread
   __shared__ __attribute__((aligned(16))) float s_scale[G * D];
-  const int h0 = blockIdx.y * G;
-  const int64_t b = blockIdx.z;
-  const int64_t tok = (int64_t)blockIdx.x * P + (threadIdx.x >> 2) / NP;
+  const int h0 = by * G;
+  const int64_t b = bz;
+  const int64_t tok = bx * P + (threadIdx.x >> 2) / NP;
   const int j = (threadIdx.x >> 2) % NP;
   const int q = threadIdx.x & 3;
   const int c = kBlock * j + 8 * q;  // the lane's first channel in the low block
@@ -267,14 +269,68 @@ __global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
   }
 }
 
+template <int D, bool PLANES>
+__global__ __launch_bounds__(256) void quantize_rope_kernel(QuantRopeArgs a) {
+  quantize_rope_block<D, PLANES>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Q-hat and K-hat with RoPE and V-hat in one launch: work-groups [0, nq) take the Q grid, the
+// next nk the K grid (each flattened x fastest), the rest the V tiles (tile fastest), so no
+// tensor waits for a kernel boundary.
 template <int D>
-static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
+__global__ __launch_bounds__(256) void quantize_qkv_rope_kernel(QuantRopeArgs qa, QuantRopeArgs ka, QuantVtArgs va,
+                                                                dim3 qg, dim3 kg, int64_t v_tiles) {
+  int64_t blk = blockIdx.x;
+  const int64_t nq = (int64_t)qg.x * qg.y * qg.z;
+  if (blk < nq) {
+    quantize_rope_block<D, false>(qa, blk % qg.x, (int)((blk / qg.x) % qg.y), blk / ((int64_t)qg.x * qg.y));
+    return;
+  }
+  blk -= nq;
+  const int64_t nk = (int64_t)kg.x * kg.y * kg.z;
+  if (blk < nk) {
+    quantize_rope_block<D, true>(ka, blk % kg.x, (int)((blk / kg.x) % kg.y), blk / ((int64_t)kg.x * kg.y));
+    return;
+  }
+  blk -= nk;
+  quantize_vt_block<D>(va, blk % v_tiles, blk / v_tiles);
+}
+
+template <int D>
+dim3 rope_grid(const QuantRopeArgs& a) {
   constexpr int p = rope_positions<D>();
   const int64_t n_tok = a.block_planes ? a.len32 : a.len;
-  dim3 grid((uint32_t)((n_tok + p - 1) / p), (uint32_t)((a.heads + kRopeHeads - 1) / kRopeHeads), (uint32_t)a.batch);
+  return dim3((uint32_t)((n_tok + p - 1) / p), (uint32_t)((a.heads + kRopeHeads - 1) / kRopeHeads), (uint32_t)a.batch);
+}
+
+template <int D>
+static hipError_t quant_rope_d(QuantRopeArgs a, hipStream_t s) {
+  const dim3 grid = rope_grid<D>(a);
   if (a.block_planes) hipLaunchKernelGGL((quantize_rope_kernel<D, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((quantize_rope_kernel<D, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t quant_qkv_rope_d(const QuantRopeArgs& qa, const QuantRopeArgs& ka, const QuantVtArgs& va,
+                                   hipStream_t s) {
+  const dim3 qg = rope_grid<D>(qa), kg = rope_grid<D>(ka);
+  const int64_t v_tiles = (va.len + vt_tokens<D>() - 1) / vt_tokens<D>();
+  const int64_t blocks = (int64_t)qg.x * qg.y * qg.z + (int64_t)kg.x * kg.y * kg.z + v_tiles * va.bh;
+  if (blocks >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_qkv_rope_kernel<D>, dim3((uint32_t)blocks), dim3(256), 0, s, qa, ka, va, qg, kg, v_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_qkv_rope(const QuantRopeArgs& qa, const QuantRopeArgs& ka, const QuantVtArgs& va,
+                                    hipStream_t s) {
+  if (qa.block_planes || !ka.block_planes || qa.d != ka.d || ka.d != va.d) return hipErrorInvalidValue;
+  switch (qa.d) {
+    case 64: return quant_qkv_rope_d<64>(qa, ka, va, s);
+    case 128: return quant_qkv_rope_d<128>(qa, ka, va, s);
+    case 256: return quant_qkv_rope_d<256>(qa, ka, va, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s) {

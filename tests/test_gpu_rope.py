@@ -92,6 +92,30 @@ def test_rope_without_smooth_qk_one_past_a_work_group():
     _case(0, False, 64, smooth_qk=False, B=1, Hq=2, Hkv=2, Lq=257, Lk=257)
 
 
+def test_rope_one_launch_equals_separate_calls():
+    """Given Q, K and V, the entry point quantizes all three in one launch; given one tensor per
+    call, it launches that tensor's quantizer alone.  Both routes must write the same bytes."""
+    import torch
+    for cfg_id, d in ((0, 64), (1, 128), (3, 256)):
+        cfg = synth.config(cfg_id, B=2, Hq=8, Hkv=2, Lq=70, Lk=190, d=d)
+        theta = cfg["rope_theta"] or 1e4
+        q, k, v = synth.make_qkv(cfg, pre_rope=True)
+        qc, kc = synth.make_calibration(cfg)
+        s32, inv32, _ = smooth.calibrate(qc, kc, cfg["alpha"], 4.0)
+        cos32, sin32 = synth.rope_table(theta, cfg["Lk"], d)
+        print("case rope one launch vs separate, d", d, flush=True)
+        dims = hf.make_dims(2, 8, 2, d, 70, 190)
+        t = dict(q=to_dev(q), k=to_dev(k), v=to_dev(v))
+        tabs = dict(s=to_dev(s32), inv_s=to_dev(inv32), rope_cos=to_dev(cos32), rope_sin=to_dev(sin32), dims=dims)
+        all3 = hf.quantize_qkv_rope(t["q"], t["k"], t["v"], **tabs)
+        for src in ("q", "k", "v"):
+            one = hf.quantize_qkv_rope(**{n: (t[n] if n == src else None) for n in ("q", "k", "v")}, **tabs)
+            torch.cuda.synchronize()
+            for name in NAMES:
+                if name[0] == src:
+                    assert torch.equal(one[name], all3[name]), "%s differs (d = %d)" % (name, d)
+
+
 def test_rope_full_size_batched_prefill():
     import torch
     cfg = synth.config(2)
