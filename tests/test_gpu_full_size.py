@@ -46,12 +46,12 @@ def _block_rows(rng, lq, block=128):
     return np.array(sorted(rows))
 
 
-def run_full(cfg_id, heads, normalizer=A.P_REORDERED, causal=None, phat_rule=A.PHAT_EXP16):
+def run_full(cfg_id, heads, normalizer=A.P_REORDERED, causal=None, phat_rule=A.PHAT_EXP16, over=None):
     """heads: list of (batch, query head, all_rows); all_rows False takes a row per 128-row block.
     causal overrides the workload's mask (the bench's non-causal legs); phat_rule selects the
-    P-hat code rule (the bench's Direct-P legs)."""
+    P-hat code rule (the bench's Direct-P legs); over overrides workload fields (e.g. B)."""
     import torch
-    cfg = dict(synth.config(cfg_id))
+    cfg = dict(synth.config(cfg_id, **(over or {})))
     if causal is not None:
         cfg["causal"] = causal
     b_n, hq, hkv, lq, lk, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Lq"], cfg["Lk"], cfg["d"]
@@ -149,3 +149,10 @@ def test_full_gemma_shaped_d256_L8192():
 def test_full_decode_B64_Lk32768():
     """Decode: every query head of batch entries 0 and 63 (a head's one row is its query)."""
     run_full(4, [(b, h, True) for b in (0, 63) for h in range(32)])
+
+
+def test_full_length_decode_small_batch():
+    """Decode at the full cache length with B = 2: automatic splits give 32 splits x 8 KV heads
+    x 2 = 512 single-wave work-groups, at most one per SIMD, so the split kernel keeps three
+    tiles in flight per wave; every query head of both batch entries."""
+    run_full(4, [(b, h, True) for b in (0, 1) for h in range(32)], over=dict(B=2, name="decode-B2-Lk32768"))
