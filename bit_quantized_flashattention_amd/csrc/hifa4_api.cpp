@@ -78,12 +78,12 @@ hifa4_status check_dims(const hifa4_dims* d) {
 
 int32_t auto_splits(const hifa4_dims* d, int kv_tile) {
   // enough (batch, KV head, split) waves to cover the 1024 SIMDs of the 256 compute units twice,
-  // or once for up to 64 (batch, KV head) units, where each wave then keeps three tiles in flight
+  // or once for up to 32 (batch, KV head) units, where each wave then keeps three tiles in flight
   // (the decode launcher's choice for grids of at most one wave per SIMD); at least 8 tiles per
   // split
   const int64_t tiles = (d->len_kv + kv_tile - 1) / kv_tile;
   const int64_t units = (int64_t)d->batch * d->heads_kv;
-  const int64_t target = units <= 64 ? 1024 : 2048;
+  const int64_t target = units <= 32 ? 1024 : 2048;
   int64_t s = (target + units - 1) / units;
   s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 8));
   s = std::max<int64_t>(1, std::min<int64_t>(s, 64));

@@ -172,6 +172,18 @@ def test_decode_splits_resolution(L):
     assert hf.decode_num_splits(hf.make_dims(1, 4, 1, 64, 9, 200), hf.make_opts()) == 1
 
 
+def test_automatic_decode_splits():
+    """The automatic split count at Lk = 32768 (256 tiles of 128 keys), Hkv = 8: one wave per SIMD
+    (1024 waves) for up to 32 (batch, KV head) units, two per SIMD (2048) above, at most 64
+    splits and at least 8 tiles per split."""
+    want = {1: 32, 2: 32, 4: 32, 8: 32, 16: 16, 32: 8, 64: 4, 128: 2}
+    for b, n in want.items():
+        d = hf.make_dims(b, 32, 8, 128, 1, 32768)
+        assert hf.decode_num_splits(d, hf.make_opts(causal=True)) == n, b
+    # a short cache: at least 8 tiles per split
+    assert hf.decode_num_splits(hf.make_dims(1, 32, 8, 128, 1, 2048), hf.make_opts(causal=True)) == 2
+
+
 def test_quantize_rejects_bad_arguments(L):
     dims = hf.make_dims(1, 4, 2, 128, 64, 64)
     dummy = ctypes.c_void_p(16)
