@@ -133,46 +133,43 @@ __device__ __forceinline__ uint32_t quantize_loaded32(const Block32In& in, bool 
 // the 32 channel scales of the block or nullptr.  A block in the first half takes
 // y = x c - x' s with x' its partner D/2 channels later; a block in the second half takes
 // y = x c + x' s with x' its partner D/2 channels earlier; each product and sum is rounded once.
-// Eight rotated and rescaled values (chunk k of the block); see quantize_block32_rope.
-__device__ __forceinline__ void rope_chunk8(const uint16_t* own, const uint16_t* partner, bool first,
-                                            const float* cos_c, const float* sin_c, const float* s, int k, float* y) {
-  const uint4 xo = *reinterpret_cast<const uint4*>(own + 8 * k);
-  const uint4 xq = *reinterpret_cast<const uint4*>(partner + 8 * k);
-  const float4 ca = *reinterpret_cast<const float4*>(cos_c + 8 * k);
-  const float4 cb = *reinterpret_cast<const float4*>(cos_c + 8 * k + 4);
-  const float4 sa = *reinterpret_cast<const float4*>(sin_c + 8 * k);
-  const float4 sb = *reinterpret_cast<const float4*>(sin_c + 8 * k + 4);
-  const uint32_t wo[4] = {xo.x, xo.y, xo.z, xo.w};
-  const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w};
-  const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-  const float ss[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-#pragma unroll
-  for (int t = 0; t < 8; t++) {
-    const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wo[t / 2] >> 16) : (wo[t / 2] & 0xFFFF)));
-    const float xp = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wq[t / 2] >> 16) : (wq[t / 2] & 0xFFFF)));
-    y[t] = first ? x * cc[t] - xp * ss[t] : x * cc[t] + xp * ss[t];
-  }
-  if (s != nullptr) {
-    const float4 ma = *reinterpret_cast<const float4*>(s + 8 * k);
-    const float4 mb = *reinterpret_cast<const float4*>(s + 8 * k + 4);
-    const float mm[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-#pragma unroll
-    for (int t = 0; t < 8; t++) y[t] = y[t] * mm[t];
-  }
-}
-
-// One pass over four chunks of eight values; the 32 results stay live for the block maximum.
+// All loads are issued before any arithmetic (one memory round trip): without Smooth-QK scales
+// the factors read are the cos entries and are replaced by 1 (y * 1 = y exactly), so no load
+// depends on a branch.
 __device__ __forceinline__ uint32_t quantize_block32_rope(const uint16_t* row, int blk, int D, const float* cos_row,
                                                           const float* sin_row, const float* s, uint4* codes) {
   const int half = D / 2;
   const int c0 = kBlock * blk;
   const bool first = c0 < half;
   const int i0 = first ? c0 : c0 - half;  // table column of the block's first channel
-  const uint16_t* own = row + c0;
-  const uint16_t* partner = row + (first ? c0 + half : c0 - half);
+  const uint4* own = reinterpret_cast<const uint4*>(row + c0);
+  const uint4* partner = reinterpret_cast<const uint4*>(row + (first ? c0 + half : c0 - half));
+  const float4* cp = reinterpret_cast<const float4*>(cos_row + i0);
+  const float4* sp = reinterpret_cast<const float4*>(sin_row + i0);
+  const float4* mp = reinterpret_cast<const float4*>(s != nullptr ? s : cos_row + i0);
+  uint4 xo[4], xq[4];
+  float4 cv[8], sv[8], mv[8];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    xo[k] = own[k];
+    xq[k] = partner[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    cv[k] = cp[k];
+    sv[k] = sp[k];
+    mv[k] = mp[k];
+  }
   float y[32];
 #pragma unroll
-  for (int k = 0; k < 4; k++) rope_chunk8(own, partner, first, cos_row + i0, sin_row + i0, s, k, y + 8 * k);
+  for (int t = 0; t < 32; t++) {
+    const uint32_t wo = (&xo[t / 8].x)[(t % 8) / 2], wq = (&xq[t / 8].x)[(t % 8) / 2];
+    const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wo >> 16) : (wo & 0xFFFF)));
+    const float xp = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (wq >> 16) : (wq & 0xFFFF)));
+    const float c = (&cv[t / 4].x)[t % 4], sn = (&sv[t / 4].x)[t % 4];
+    const float m = s != nullptr ? (&mv[t / 4].x)[t % 4] : 1.0f;
+    y[t] = (first ? x * c - xp * sn : x * c + xp * sn) * m;
+  }
   return quantize_values32(y, codes);
 }
 

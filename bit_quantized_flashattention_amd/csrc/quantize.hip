@@ -352,35 +352,58 @@ hipError_t launch_quantize_rope(QuantRopeArgs a, hipStream_t s) {
 template <int D>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheAppendArgs a) {
   constexpr int NB = D / kBlock;
+  constexpr int SI = kBlock * D / 256;  // stage elements per thread at most (256 threads)
   const int64_t bh = blockIdx.x;
   const int h = (int)(bh % a.heads_kv);
   const int64_t end = a.len0 + a.n;
-  // K-hat: one thread per (new key, 32-channel block)
-  for (int64_t it = threadIdx.x; it < a.n * NB; it += blockDim.x) {
-    const int blk = (int)(it % NB);
-    const int64_t t = it / NB, pos = a.len0 + t;
-    const uint16_t* x = a.k_new + (bh * a.n + t) * D;
-    const float* sc = a.inv_s ? a.inv_s + (int64_t)h * D + kBlock * blk : nullptr;
-    uint4 out;
-    const uint32_t e8 = a.rope_cos ? quantize_block32_rope(x, blk, D, a.rope_cos + pos * (D / 2),
-                                                           a.rope_sin + pos * (D / 2), sc, &out)
-                                   : quantize_block32(x + kBlock * blk, sc, &out);
-    *reinterpret_cast<uint4*>(a.k_codes + (bh * a.rows + pos) * (D / 2) + 16 * blk) = out;
-    a.k_scales[(bh * NB + blk) * a.rows32 + pos] = (uint8_t)e8;
+  // K-hat: one thread per (new key, 32-channel block), on the threads the V-hat blocks leave
+  // idle where there are any (d < 256), so the two parts' loads are in flight together
+  constexpr int KT0 = D < 256 ? D : 0;
+  if (threadIdx.x >= KT0) {
+    for (int64_t it = threadIdx.x - KT0; it < a.n * NB; it += blockDim.x - KT0) {
+      const int blk = (int)(it % NB);
+      const int64_t t = it / NB, pos = a.len0 + t;
+      const uint16_t* x = a.k_new + (bh * a.n + t) * D;
+      const float* sc = a.inv_s ? a.inv_s + (int64_t)h * D + kBlock * blk : nullptr;
+      uint4 out;
+      const uint32_t e8 = a.rope_cos ? quantize_block32_rope(x, blk, D, a.rope_cos + pos * (D / 2),
+                                                             a.rope_sin + pos * (D / 2), sc, &out)
+                                     : quantize_block32(x + kBlock * blk, sc, &out);
+      *reinterpret_cast<uint4*>(a.k_codes + (bh * a.rows + pos) * (D / 2) + 16 * blk) = out;
+      a.k_scales[(bh * NB + blk) * a.rows32 + pos] = (uint8_t)e8;
+    }
   }
-  // V-hat: every touched 32-key block, one thread per channel
+  // V-hat: every touched 32-key block, one thread per channel.  An element's source (the stage,
+  // the new keys, or the zero padding past the last key) depends only on its position, the same
+  // for every thread: the row is picked by uniform arithmetic, and the block's loads are in
+  // flight together (padding inside a group of 8 reads the stage's first row and becomes 0)
   const int64_t open0 = a.len0 - a.len0 % kBlock;  // first key of the block that was open
   for (int64_t jb = a.len0 / kBlock; jb * kBlock < end; jb++) {
     for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
+      uint32_t bits[32];
+#pragma unroll
+      for (int g8 = 0; g8 < 4; g8++) {
+        if (jb * kBlock + 8 * g8 < end) {  // groups of 8 wholly past the last key are not read
+#pragma unroll
+          for (int i = 8 * g8; i < 8 * g8 + 8; i++) {
+            const int64_t p = jb * kBlock + i;
+            const uint16_t* src = p < a.len0 ? a.v_stage + (bh * kBlock + (p - open0)) * D
+                                             : (p < end ? a.v_new + (bh * a.n + (p - a.len0)) * D
+                                                        : a.v_stage + bh * kBlock * D);
+            bits[i] = src[ch];
+          }
+        } else {
+#pragma unroll
+          for (int i = 8 * g8; i < 8 * g8 + 8; i++) bits[i] = 0u;
+        }
+      }
+      // every value is needed here, so no conversion (and wait) moves into the branches above
+#pragma unroll
+      for (int i = 0; i < 32; i++) asm volatile("" ::"v"(bits[i]));
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; i++) {
-        const int64_t p = jb * kBlock + i;
-        uint16_t bits = 0;
-        if (p < a.len0) bits = a.v_stage[(bh * kBlock + (p - open0)) * D + ch];
-        else if (p < end) bits = a.v_new[(bh * a.n + (p - a.len0)) * D + ch];
-        v[i] = (float)__builtin_bit_cast(_Float16, bits);
-      }
+      for (int i = 0; i < 32; i++)
+        v[i] = jb * kBlock + i < end ? (float)__builtin_bit_cast(_Float16, (uint16_t)bits[i]) : 0.0f;
       uint4 out;
       const uint32_t e8 = quantize_values32(v, &out);
       const int64_t blk_row = (bh * (a.rows32 / kBlock) + jb) * D;
@@ -388,14 +411,24 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheAppendArgs a) {
       a.v_scales[blk_row + (D / 16) * (ch % 16) + ch / 16] = (uint8_t)e8;
     }
   }
-  __syncthreads();
-  // the block left open: its keys (FP16) go to the stage for the next append
+  // the block left open: its keys (FP16) go to the stage for the next append.  The new keys are
+  // read before the barrier; the stage is written after it, once every read of the old stage is
+  // done.  Keys before len0 are in the stage already, in the same slot.
   const int64_t open1 = end - end % kBlock;
-  for (int64_t it = threadIdx.x; it < (end - open1) * D; it += blockDim.x) {
+  const int cnt = (int)((end - open1) * D);
+  uint16_t sv[SI];
+#pragma unroll
+  for (int k = 0; k < SI; k++) {
+    const int it = (int)threadIdx.x + 256 * k;
     const int64_t p = open1 + it / D;
-    const int ch = (int)(it % D);
-    if (p >= a.len0)  // keys before len0 are in the stage already, in the same slot
-      a.v_stage[(bh * kBlock + (p - open1)) * D + ch] = a.v_new[(bh * a.n + (p - a.len0)) * D + ch];
+    sv[k] = it < cnt && p >= a.len0 ? a.v_new[(bh * a.n + (p - a.len0)) * D + it % D] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SI; k++) {
+    const int it = (int)threadIdx.x + 256 * k;
+    const int64_t p = open1 + it / D;
+    if (it < cnt && p >= a.len0) a.v_stage[(bh * kBlock + (p - open1)) * D + it % D] = sv[k];
   }
 }
 
