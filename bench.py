@@ -25,6 +25,13 @@ leg, median, min and max.  Rates: algorithmic FLOPs are 4 * d per visible (query
 (L(L+1)/2 pairs per head when causal); decode bytes are the K-hat/V-hat codes and scales, the
 FP16 query, the Smooth-QK scales and the FP16 output.  Peaks: MI355X dense FP4 MFMA
 10.1 PFLOP/s, HBM3E 8 TB/s (AMD's published figures).
+
+roofline.traffic (HBM bytes per launch of the leg's dominant kernels) and the matrix-core and
+vector-ALU busy fractions come from three rocprofv3 --pmc runs of this script started after the
+timed legs (FETCH_SIZE; WRITE_SIZE; SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_VALU and
+GRBM_GUI_ACTIVE), each two steps of the headline, d256, Direct-P and decode legs plus a plain
+512 MiB device copy that scales the byte counters.  --counters stored takes them from
+profiles/counters.json instead when its kernel sources are these; "counters.source" says which.
 """
 import argparse
 import json
@@ -45,6 +52,15 @@ KERNEL_SOURCES = ["attn_prefill.hip", "attn_decode.hip", "device_common.h", "qua
 ALL_LEGS = ["prefill_d256", "direct_p", "noncausal", "rope_prefill", "decode"]
 
 
+def progress(msg):
+    """One progress line on stderr (stdout carries only the JSON line)."""
+    sys.stderr.write("bench: %s (%.0f s)\n" % (msg, time.perf_counter() - T0))
+    sys.stderr.flush()
+
+
+T0 = time.perf_counter()
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -58,6 +74,10 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="also run one plain %d MiB device copy (counter calibration for HBM traffic)"
                         % (COPY_PROBE_BYTES >> 20))
+    p.add_argument("--counters", choices=["live", "stored", "none"], default="live",
+                   help="HBM traffic and busy fractions of the rooflines: measured now by rocprofv3 runs of "
+                        "this script (live), taken from profiles/counters.json when its kernel sources match "
+                        "(stored), or left out")
     a = p.parse_args()
     legs = [x for x in a.legs.split(",") if x]
     if a.no_decode and "decode" in legs:
@@ -117,6 +137,147 @@ def copy_probe():
     torch.cuda.empty_cache()
 
 
+# The dominant kernels of the legs whose rooflines carry counter figures (demangled-name
+# substrings; decode counts its split and merge launches together).
+COUNTER_KERNELS = {
+    "prefill": ["attn_prefill_kernel<128, true, 0, false, 0>"],
+    "prefill_d256": ["attn_prefill_kernel<256, true, 0, false, 0>"],
+    "direct_p": ["attn_prefill_kernel<128, true, 0, false, 2>"],
+    "decode": ["attn_decode_split_kernel<128, 0, 0, 2>", "attn_decode_merge_kernel<128>"],
+}
+COUNTER_RUNS = [["FETCH_SIZE"], ["WRITE_SIZE"], ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"]]
+N_SIMDS = 1024  # 256 compute units x 4
+
+
+def profiled_run(counters, timeout_s=300):
+    """Runs this script (the headline, d256, Direct-P and decode legs, two timed steps each, and
+    the copy probe) under rocprofv3 --pmc with the given counters; returns {kernel name: {counter:
+    [value per dispatch]}} or None.  The child's own JSON line is discarded."""
+    import glob
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    exe = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(exe):
+        return None
+    out = tempfile.mkdtemp(prefix="hifa4_ctr_")
+    cmd = [exe, "--pmc"] + counters + ["--output-format", "csv", "-d", out, "-o", "c", "--",
+                                       sys.executable, os.path.abspath(__file__), "--steps", "2", "--warmup", "1",
+                                       "--no-cpu-baseline", "--counters", "none", "--traffic-probe",
+                                       "--legs", "prefill_d256,direct_p,decode"]
+    env = dict(os.environ, TMPDIR=out)
+    progress("counter run %s" % " ".join(counters))
+    proc = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, env=env, cwd=out,
+                            start_new_session=True)
+    try:
+        _, err = proc.communicate(timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        os.killpg(proc.pid, signal.SIGKILL)  # the profiler and the child it started, nothing else
+        proc.communicate()
+        shutil.rmtree(out, ignore_errors=True)
+        return None
+    files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
+    if proc.returncode != 0 or not files:
+        sys.stderr.write("counter run %s failed (rc %d): %s\n" % (counters, proc.returncode, err.decode()[-500:]))
+        shutil.rmtree(out, ignore_errors=True)
+        return None
+    res = parse_counter_csv(files[0])
+    shutil.rmtree(out, ignore_errors=True)
+    return res
+
+
+def parse_counter_csv(path):
+    """{kernel name: {counter: [value per dispatch, in dispatch order]}} of a rocprofv3
+    counter_collection.csv; a dispatch's rows (one per counter and hardware instance) are summed."""
+    import csv
+    per_disp, names = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = per_disp.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    res = {}
+    for disp in sorted(per_disp, key=int):
+        for c, v in per_disp[disp].items():
+            res.setdefault(names[disp], {}).setdefault(c, []).append(v)
+    return res
+
+
+def live_counters():
+    """HBM bytes per launch and matrix/vector busy fractions of each leg's dominant kernel(s),
+    measured in this run: three profiled runs of this script, one per counter group (a counter
+    group needs a run of its own).  None when the profiler is missing or a run fails."""
+    runs = []
+    for counters in COUNTER_RUNS:
+        r = profiled_run(counters)
+        if r is None:
+            return None
+        runs.append(r)
+    return derive_counters(runs)
+
+
+def derive_counters(runs):
+    """From the three parsed runs (FETCH_SIZE; WRITE_SIZE; the busy counters): per leg, the mean
+    per dispatch of FETCH_SIZE and WRITE_SIZE (KiB) scaled by bytes / counter of the run's largest
+    device copy (the 512 MiB probe), summed over the leg's kernels, and the busy fractions of its
+    first kernel over 1024 SIMDs and the kernel's cycles (GRBM_GUI_ACTIVE / 8 XCDs)."""
+
+    def mean(run, sub, counter):
+        vals = [v for name, cs in run.items() if sub in name for v in cs.get(counter, [])]
+        return sum(vals) / len(vals) if vals else None
+
+    # the probe is the run's largest device copy: its dispatch, not a mean over smaller copies
+    f_copy = max([v for name, cs in runs[0].items() if "copyBuffer" in name for v in cs.get("FETCH_SIZE", [])] or [0.0])
+    w_copy = max([v for name, cs in runs[1].items() if "copyBuffer" in name for v in cs.get("WRITE_SIZE", [])] or [0.0])
+    if f_copy <= 0.0 or w_copy <= 0.0:
+        return None
+    f_scale, w_scale = COPY_PROBE_BYTES / (f_copy * 1024.0), COPY_PROBE_BYTES / (w_copy * 1024.0)
+    out = {}
+    for key, subs in COUNTER_KERNELS.items():
+        fetch = [mean(runs[0], sub, "FETCH_SIZE") for sub in subs]
+        write = [mean(runs[1], sub, "WRITE_SIZE") for sub in subs]
+        if None in fetch or None in write:
+            continue
+        k = {"traffic": int(round(sum(fetch) * 1024.0 * f_scale + sum(write) * 1024.0 * w_scale)),
+             "fetch_bytes": int(round(sum(fetch) * 1024.0 * f_scale)), "write_bytes": int(round(sum(write) * 1024.0 * w_scale))}
+        g = mean(runs[2], subs[0], "GRBM_GUI_ACTIVE")
+        mb, va = mean(runs[2], subs[0], "SQ_VALU_MFMA_BUSY_CYCLES"), mean(runs[2], subs[0], "SQ_ACTIVE_INST_VALU")
+        if g and mb is not None and va is not None:
+            cyc = g / 8.0  # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+            k["mfma_busy"] = round(mb / (N_SIMDS * cyc), 4)
+            k["valu_busy"] = round(4.0 * va / (N_SIMDS * cyc), 4)
+        out[key] = k
+    out["_scale"] = {"copy_bytes": COPY_PROBE_BYTES, "fetch_factor": round(f_scale, 4), "write_factor": round(w_scale, 4)}
+    return out
+
+
+def add_counters(line, mode):
+    """Fills traffic (and the busy fractions) into the rooflines of the headline, d256, Direct-P
+    and decode legs, from live counter runs or the stored ones; records which."""
+    rooflines = {"prefill": line.get("roofline"), "prefill_d256": line.get("prefill_d256", {}).get("roofline"),
+                 "direct_p": line.get("direct_p", {}).get("roofline"), "decode": line.get("decode", {}).get("roofline")}
+    ctr, source = None, None
+    if mode == "live":
+        ctr = live_counters()
+        source = "live: rocprofv3 --pmc runs of this script in this run" if ctr else None
+    if ctr is None and mode in ("live", "stored"):
+        ctr = {k: counters_for(k) for k in rooflines}
+        if any(ctr.values()):
+            source = "stored: profiles/counters.json (taken on these kernel sources)"
+        else:
+            ctr = None
+    for key, rf in rooflines.items():
+        c = (ctr or {}).get(key)
+        if rf is None or not c:
+            continue
+        rf["traffic"] = c.get("traffic")
+        for name in ("mfma_busy", "valu_busy"):
+            if name in c:
+                rf[name] = c[name]
+    line["counters"] = {"source": source, "scale": (ctr or {}).get("_scale")}
+
+
 def causal_pairs(lq, lk):
     shift = lk - lq
     return sum(min(lk, r + shift + 1) for r in range(lq))
@@ -152,19 +313,15 @@ def spread(ms):
             "min": round(min(ms), 4), "max": round(max(ms), 4)}
 
 
-def mfma_roofline(flops, kernel_ms, counters):
+def mfma_roofline(flops, kernel_ms):
+    """Roofline against the dense FP4 peak; traffic (and the busy fractions) are filled in by
+    add_counters once the counter runs are done."""
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-         "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 4)}
-    if counters:
-        r["traffic"] = counters.get("traffic")
-        if "mfma_busy" in counters:
-            r["mfma_busy"] = counters["mfma_busy"]
-            r["valu_busy"] = counters.get("valu_busy")
-    return r
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 4)}
 
 
-def bench_prefill(args, cfg_id, causal=None, phat_rule=0, counter_key=None):
+def bench_prefill(args, cfg_id, causal=None, phat_rule=0):
     """One prefill leg: per step, K/V quantize, then the attention with Q quantized in-kernel."""
     import torch
     import bit_quantized_flashattention_amd as hf
@@ -207,7 +364,7 @@ def bench_prefill(args, cfg_id, causal=None, phat_rule=0, counter_key=None):
         "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
         "attention_ms": spread(attn),
         "quantize_kv_ms": spread(quant),
-        "roofline": mfma_roofline(flops, attn_ms, counters_for(counter_key) if counter_key else None),
+        "roofline": mfma_roofline(flops, attn_ms),
     }
     extra = dict(cfg=cfg, gate=gate, step_ms=step_ms, flops=flops)
     del q, k, v, qkv, out
@@ -347,7 +504,6 @@ def bench_decode(args):
     q_bytes = b * hq * d * 2 + hkv * d * 4  # FP16 query and the Smooth-QK scales
     out_bytes = b * hq * d * 2
     total = kv_bytes + q_bytes + out_bytes
-    ctr = counters_for("decode")
     res = {
         "workload": "split-KV decode B%d Hq%d/Hkv%d d%d Lk%d, 4-bit cache, %d splits" % (b, hq, hkv, d, lk, splits),
         "metric": "decode HBM GB/s",
@@ -358,7 +514,7 @@ def bench_decode(args):
         "kernel_ms": spread(attn),
         "roofline": {"bound": "hbm", "achieved": round(total / (attn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(total / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": ctr.get("traffic") if ctr else None, "kernel_us": round(attn_ms * 1e3, 1)},
+                     "traffic": None, "kernel_us": round(attn_ms * 1e3, 1)},
     }
     del qkv, ws, out, q, k, v
     torch.cuda.empty_cache()
@@ -439,7 +595,8 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
-    pre, ex = bench_prefill(args, 2, counter_key="prefill")
+    pre, ex = bench_prefill(args, 2)
+    progress("headline prefill leg done")
     cfg = ex["cfg"]
     line = {
         "metric": "4-bit attention fwd TFLOP/s (+% FP4-MFMA peak); decode HBM GB/s",
@@ -465,9 +622,9 @@ def main():
         "quantize_kv_ms": pre["quantize_kv_ms"],
     }
     if "prefill_d256" in args.leg_list:
-        line["prefill_d256"] = bench_prefill(args, 3, counter_key="prefill_d256")[0]
+        line["prefill_d256"] = bench_prefill(args, 3)[0]
     if "direct_p" in args.leg_list:
-        line["direct_p"] = bench_prefill(args, 2, phat_rule=1, counter_key="direct_p")[0]
+        line["direct_p"] = bench_prefill(args, 2, phat_rule=1)[0]
     if "noncausal" in args.leg_list:
         line["noncausal"] = {"exp16": bench_prefill(args, 2, causal=False)[0],
                              "direct_p": bench_prefill(args, 2, causal=False, phat_rule=1)[0]}
@@ -476,9 +633,15 @@ def main():
     if "decode" in args.leg_list:
         line["decode"] = bench_decode(args)
         line["decode"]["cache_append"] = bench_append(args)
+    progress("legs done: %s" % ",".join(args.leg_list))
     if args.traffic_probe:
         copy_probe()
+    if args.counters != "none":
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        add_counters(line, args.counters)
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         torch.cuda.synchronize()
         line["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(line), flush=True)
