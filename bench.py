@@ -149,7 +149,7 @@ COUNTER_RUNS = [["FETCH_SIZE"], ["WRITE_SIZE"], ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ
 N_SIMDS = 1024  # 256 compute units x 4
 
 
-def profiled_run(counters, timeout_s=300):
+def profiled_run(counters, timeout_s=150):
     """Runs this script (the headline, d256, Direct-P and decode legs, two timed steps each, and
     the copy probe) under rocprofv3 --pmc with the given counters; returns {kernel name: {counter:
     [value per dispatch]}} or None.  The child's own JSON line is discarded."""
