@@ -140,9 +140,9 @@ def copy_probe():
 # The dominant kernels of the legs whose rooflines carry counter figures (demangled-name
 # substrings; decode counts its split and merge launches together).
 COUNTER_KERNELS = {
-    "prefill": ["attn_prefill_kernel<128, true, 0, false, 0>"],
-    "prefill_d256": ["attn_prefill_kernel<256, true, 0, false, 0>"],
-    "direct_p": ["attn_prefill_kernel<128, true, 0, false, 2>"],
+    "prefill": ["attn_prefill_kernel<128, true, 0, false, 0, 8>"],
+    "prefill_d256": ["attn_prefill_kernel<256, true, 0, false, 0, 8>"],
+    "direct_p": ["attn_prefill_kernel<128, true, 0, false, 2, 8>"],
     "decode": ["attn_decode_split_kernel<128, 0, 0, 2>", "attn_decode_merge_kernel<128>"],
 }
 COUNTER_RUNS = [["FETCH_SIZE"], ["WRITE_SIZE"], ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"]]

@@ -34,7 +34,7 @@ class Dims(ctypes.Structure):
 class Opts(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("normalizer", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("kv_capacity", ctypes.c_int64), ("max_rule", ctypes.c_int32),
-                ("phat_scale", ctypes.c_int32), ("phat_rule", ctypes.c_int32)]
+                ("phat_scale", ctypes.c_int32), ("phat_rule", ctypes.c_int32), ("prefill_waves", ctypes.c_int32)]
 
 
 _lib = None
@@ -97,9 +97,9 @@ def make_dims(batch, heads_q, heads_kv, head_dim, len_q, len_kv):
 
 
 def make_opts(causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0, kv_capacity=0, max_rule=0,
-              phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
+              phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16, prefill_waves=0):
     return Opts(int(causal), int(normalizer), int(kv_tile), int(num_splits), int(kv_capacity), int(max_rule),
-                int(phat_scale), int(phat_rule))
+                int(phat_scale), int(phat_rule), int(prefill_waves))
 
 
 def _ptr(t):
@@ -269,7 +269,7 @@ def stats_shape(dims, kv_tile):
 
 def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, num_splits=0,
                   out=None, workspace=None, tile_stats=None, stream=None, q16=None, kv_capacity=0,
-                  max_rule=MAX_CEIL, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16):
+                  max_rule=MAX_CEIL, phat_scale=PHAT_BLOCK32, phat_rule=PHAT_EXP16, prefill_waves=0):
     """4-bit attention forward from quantized operands (a dict as returned by quantize_qkv).
 
     ``q16=(q, s)`` or ``(q, s, rope_cos, rope_sin)``: take FP16 Q (before RoPE when the tables are
@@ -280,12 +280,15 @@ def attention_fwd(qkv, dims, causal=False, normalizer=P_REORDERED, kv_tile=128, 
     (round-to-nearest running max, an accuracy variant; prefill, P-Reordered, no tile statistics).
     ``phat_scale``: PHAT_BLOCK32 (the method) or PHAT_TILE; ``phat_rule``: PHAT_EXP16 (the method) or
     PHAT_DIRECT (Direct-P codes); the variants run P-Reordered without tile statistics.
+    ``prefill_waves``: 0 (automatic), 4 or 8 waves per prefill work-group (the output does not
+    depend on it).
 
     Returns the FP16 output [B, Hq, Lq, d] (``out`` if given).  ``tile_stats``: True to allocate,
     or an FP32 tensor of ``stats_shape`` to fill (prefill only); returned as a second value.
     """
     import torch
-    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule, phat_scale, phat_rule)
+    opts = make_opts(causal, normalizer, kv_tile, num_splits, kv_capacity, max_rule, phat_scale, phat_rule,
+                     prefill_waves)
     dev = qkv["k_codes"].device
     if out is None:
         out = torch.empty((dims.batch, dims.heads_q, dims.len_q, dims.head_dim), dtype=torch.float16, device=dev)

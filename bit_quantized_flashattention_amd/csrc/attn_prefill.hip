@@ -44,11 +44,14 @@ constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wav
 #ifndef PREFILL_STAGES
 #define PREFILL_STAGES 2
 #endif
+#ifndef PREFILL_SMALL_GRID_WAVES
+#define PREFILL_SMALL_GRID_WAVES 4  // waves per work-group of grids too small to fill the chip (0: off)
+#endif
 constexpr int kStages = PREFILL_STAGES;  // LDS ring depth (2: tile j+1 streams in while j is used)
 
-template <int D>
+template <int D, int WAVES = PREFILL_WAVES>
 struct Cfg {
-  static constexpr int kWaves = PREFILL_WAVES;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKSteps = D >= 128 ? D / 128 : 1;  // MFMA contractions over d
   static constexpr int kCB = D / 16;                      // 16-channel output blocks
@@ -200,10 +203,10 @@ __device__ __forceinline__ void issue_one(const Slices& sl, int sec, uint32_t ds
 // Load I of wave w is stage load w + W I; where all waves' loads I fall in one section, that
 // section is known at compile time and the load needs no branch.  LDS addresses are computed
 // from the (scalar) wave index, so they need no vector work.
-template <int D, int I = 0>
+template <int D, int WAVES, int I = 0>
 __device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, int wave_u, int n, uint32_t stage,
                                            int k0) {
-  using C = Cfg<D>;
+  using C = Cfg<D, WAVES>;
   constexpr int W = C::kWaves;
   if constexpr (I < C::kMaxLoadsPerWave) {
     const int j = wave_u + W * I;
@@ -214,7 +217,7 @@ __device__ __forceinline__ void issue_tile(const Slices& sl, const LoadOp* ops, 
       if (I >= n) return;
       issue_one<D>(sl, load_section<D>(j), stage + load_lds<D>(j), ops[I].voff, k0);
     }
-    issue_tile<D, I + 1>(sl, ops, wave_u, n, stage, k0);
+    issue_tile<D, WAVES, I + 1>(sl, ops, wave_u, n, stage, k0);
   }
 }
 
@@ -248,13 +251,15 @@ __device__ __forceinline__ const float* q_smooth_blk(const AttnArgs& a, int kvh,
 // PH: the P-hat rule: 0 = one scale per (row, 32-key block), codes from the FP16 probabilities
 // (the method); 1 = one scale per (row, tile) (accuracy variant); 2 = Direct-P codes, one scale
 // per (row, 32-key block)
-template <int D, bool CAUSAL, int MODE, bool STATS, int PH>
-__global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_MIN_WAVES : 4) void attn_prefill_kernel(AttnArgs a) {
-  using Cf = Cfg<D>;
+// The 8-wave instances keep their registers at the 6-waves-per-SIMD budget; the small-grid ones
+// (4 waves per work-group) are held by LDS to 4 waves per SIMD, and their budget says so.
+template <int D, bool CAUSAL, int MODE, bool STATS, int PH, int WAVES = PREFILL_WAVES>
+__global__ __launch_bounds__(WAVES * 64, (MODE == 0 && !STATS && WAVES == PREFILL_WAVES) ? PREFILL_MIN_WAVES : 4) void attn_prefill_kernel(AttnArgs a) {
+  using Cf = Cfg<D, WAVES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * Cf::kStageBytes];
   constexpr int W = Cf::kWaves;
   constexpr int KSTEPS = Cf::kKSteps;
   constexpr int CB = Cf::kCB;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * Cf::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
   // prologue: tiles 0 .. kStages-2 in flight, wait for tile 0
 #pragma unroll
   for (int p = 0; p < kStages - 1; p++)
-    if (p < n_tiles) issue_tile<D>(sl, ops, wave_u, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
+    if (p < n_tiles) issue_tile<D, WAVES>(sl, ops, wave_u, n_loads, smem_lds + p * Cf::kStageBytes, p * bc);
   if (fused_q) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (MODE == 0 && !STATS) ? PREFILL_M
     const int k0 = tile * bc;
     const uint8_t* T = smem + (tile % kStages) * Cf::kStageBytes;
     const int ahead = tile + kStages - 1;
-    if (ahead < n_tiles) issue_tile<D>(sl, ops, wave_u, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
+    if (ahead < n_tiles) issue_tile<D, WAVES>(sl, ops, wave_u, n_loads, smem_lds + (ahead % kStages) * Cf::kStageBytes, ahead * bc);
 
     if (wave_live && !(CAUSAL && k0 > wave_last + shift)) {
       // ---- S^T = K-hat Q-hat^T: MFMA t takes key score_row_key(t, r) as row r; its operands sit
@@ -576,16 +581,46 @@ int gcd_int(int x, int y) {
   return x;
 }
 
-template <int D, bool CAUSAL, int MODE, bool STATS, int PH = 0>
-hipError_t launch4(AttnArgs a, hipStream_t s) {
-  constexpr int W = Cfg<D>::kWaves;
+// Grid of WAVES-wave work-groups: gcd(group, WAVES) query heads each, 16 * WAVES / heads rows of each
+template <int D, int WAVES>
+dim3 prefill_grid(AttnArgs& a) {
   const int group = a.heads_q / a.heads_kv;
-  const int hw = gcd_int(group, W);  // query heads per work-group
-  const int bq = 16 * (W / hw);
+  const int hw = gcd_int(group, WAVES);  // query heads per work-group
+  const int bq = 16 * (WAVES / hw);
   a.heads_per_wg = hw;
   const int64_t qblocks = (a.len_q + bq - 1) / bq;
-  dim3 grid((uint32_t)qblocks, (uint32_t)(a.heads_kv * (group / hw)), (uint32_t)a.batch);
-  hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS, PH>), grid, dim3(Cfg<D>::kThreads), 0, s, a);
+  return dim3((uint32_t)qblocks, (uint32_t)(a.heads_kv * (group / hw)), (uint32_t)a.batch);
+}
+
+// Work-groups of the default shape that fit on the chip at once: 256 compute units, each with
+// room (registers and LDS) for three 8-wave work-groups at d <= 128.
+constexpr int64_t kResidentWorkGroups = 256 * 3;
+
+template <int D, bool CAUSAL, int MODE, bool STATS, int PH = 0>
+hipError_t launch4(AttnArgs a, hipStream_t s) {
+  // A causal grid of 8-wave work-groups that fills the chip at most once (short or
+  // single-sequence prefill) leaves SIMDs idle, and its blocks, whose lengths differ by up to the
+  // whole key range, finish unevenly.  The method's P-Reordered instance then runs 4-wave
+  // work-groups: twice as many, each holding one wave per SIMD, so more SIMDs share the heavy
+  // blocks (d128, Hq32/Hkv8: B1 L2048 33.8 -> 30.6 us, B1 L3072 57.4 -> 51.8 us, B2 L1024 26.6 ->
+  // 22.7 us; at 1024 8-wave work-groups, B2 L2048, 8 waves stay 9 % faster).  A non-causal grid has
+  // no such imbalance and keeps 8 waves, whose K/V tiles serve twice the rows (B1 L2048: 4 waves
+  // 45.1 us, 8 waves 42.7 us).  Each wave computes the same 16 rows over the same tiles either
+  // way, so the output is bit-identical.  opts.prefill_waves overrides the choice.
+  if constexpr (PREFILL_SMALL_GRID_WAVES > 0 && D <= 128 && MODE == 0 && !STATS && PH == 0) {
+    AttnArgs big = a;
+    const dim3 g = prefill_grid<D, PREFILL_WAVES>(big);
+    const bool small = CAUSAL && (int64_t)g.x * g.y * g.z <= kResidentWorkGroups;
+    if (a.wg_waves == PREFILL_SMALL_GRID_WAVES || (a.wg_waves == 0 && small)) {
+      const dim3 gs = prefill_grid<D, PREFILL_SMALL_GRID_WAVES>(a);
+      hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS, PH, PREFILL_SMALL_GRID_WAVES>), gs,
+                         dim3(PREFILL_SMALL_GRID_WAVES * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.wg_waves != 0 && a.wg_waves != PREFILL_WAVES) return hipErrorInvalidValue;  // checked by the API
+  const dim3 g = prefill_grid<D, PREFILL_WAVES>(a);
+  hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS, PH>), g, dim3(Cfg<D>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -108,6 +108,12 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
       (o->normalizer != HIFA4_P_REORDERED || o->max_rule != HIFA4_MAX_CEIL))
     return fail(HIFA4_ERR_UNSUPPORTED, "the P-hat variants run P-Reordered with HIFA4_MAX_CEIL");
   if (o->num_splits < 0 || o->num_splits > 256) return fail(HIFA4_ERR_SHAPE, "num_splits must be in [0, 256]");
+  if (o->prefill_waves != 0 && o->prefill_waves != 4 && o->prefill_waves != 8)
+    return fail(HIFA4_ERR_SHAPE, "prefill_waves must be 0, 4 or 8");
+  if (o->prefill_waves == 4 && d->len_q > 1 &&
+      (d->head_dim > 128 || o->normalizer != HIFA4_P_REORDERED || o->max_rule != HIFA4_MAX_CEIL ||
+       o->phat_rule != HIFA4_PHAT_EXP16 || o->phat_scale != HIFA4_PHAT_BLOCK32))
+    return fail(HIFA4_ERR_UNSUPPORTED, "prefill_waves = 4 runs d <= 128 with the method's P-Reordered rules only");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
   if (o->kv_capacity != 0 &&
       (o->kv_capacity < d->len_kv || round32(o->kv_capacity) * (d->head_dim / 2) >= (int64_t(1) << 31)))
@@ -374,6 +380,7 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
   a.normalizer = opts->normalizer;
   a.max_rule = opts->max_rule;
   a.phat = opts->phat_rule == HIFA4_PHAT_DIRECT ? 2 : (opts->phat_scale == HIFA4_PHAT_TILE ? 1 : 0);
+  a.wg_waves = opts->prefill_waves;
   a.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
   hipStream_t stream = (hipStream_t)hip_stream;
   hipError_t e;
@@ -385,6 +392,8 @@ hifa4_status attention_launch(hifa4::AttnArgs& a, const hifa4_dims* dims, const 
   }
   if (a.stats && a.phat != 0)
     return fail(HIFA4_ERR_UNSUPPORTED, "attention: the P-hat variants run without tile statistics");
+  if (a.stats && a.wg_waves == 4 && dims->len_q > 1)
+    return fail(HIFA4_ERR_UNSUPPORTED, "attention: prefill_waves = 4 runs without tile statistics");
   if (dims->len_q == 1) {
     if (a.stats) return fail(HIFA4_ERR_UNSUPPORTED, "attention: tile_stats is prefill-only");
     const size_t need = hifa4_attention_workspace_bytes(dims, opts);

@@ -60,6 +60,7 @@ struct AttnArgs {
   int32_t num_splits;
   int32_t tiles_per_split;
   int32_t heads_per_wg;  // prefill: query heads served by one work-group (set by the launcher)
+  int32_t wg_waves;      // prefill: requested waves per work-group (0 automatic, 4 or 8)
   float c_log2;         // fp32(log2(e) / sqrt(d)); the kernels use the same value as a constant per d
 };
 

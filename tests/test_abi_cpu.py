@@ -102,9 +102,9 @@ def test_attention_rejects_bad_arguments_without_launching(L):
 
 def test_max_rule_is_validated_and_limited_to_prefill(L):
     # hifa4_attn_opts: four int32, the int64 capacity at offset 16, max_rule at 24, phat_scale at
-    # 28, phat_rule at 32, padded to 40
+    # 28, phat_rule at 32, prefill_waves at 36: 40 bytes
     assert ctypes.sizeof(hf.Opts) == 40 and hf.Opts.max_rule.offset == 24
-    assert hf.Opts.phat_scale.offset == 28 and hf.Opts.phat_rule.offset == 32
+    assert hf.Opts.phat_scale.offset == 28 and hf.Opts.phat_rule.offset == 32 and hf.Opts.prefill_waves.offset == 36
     dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     pre = hf.make_dims(1, 4, 2, 128, 64, 64)
     st = L.hifa4_attention_fwd(ctypes.byref(pre), ctypes.byref(hf.make_opts(max_rule=2)), *([dummy] * 7), None, 0, None, None)
@@ -137,6 +137,25 @@ def test_phat_options_are_validated(L):
         assert call(o) == 3 and b"P-Reordered" in L.hifa4_last_error()
     stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
     assert call(hf.make_opts(phat_rule=hf.PHAT_DIRECT), stats) == 3 and b"statistics" in L.hifa4_last_error()
+
+
+def test_prefill_waves_is_validated(L):
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    pre = hf.make_dims(1, 4, 2, 128, 64, 64)
+
+    def call(o, dims=pre, stats=None):
+        return L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(o), *([dummy] * 7), None, 0, stats, None)
+    for w in (1, 2, 6, 16, -4):
+        assert call(hf.make_opts(prefill_waves=w)) == 2 and b"prefill_waves" in L.hifa4_last_error()
+    # 4-wave work-groups exist for the method's P-Reordered instance at d <= 128 only
+    for o in [hf.make_opts(prefill_waves=4, normalizer=hf.INCONSISTENT),
+              hf.make_opts(prefill_waves=4, max_rule=hf.MAX_NEAREST16),
+              hf.make_opts(prefill_waves=4, phat_rule=hf.PHAT_DIRECT),
+              hf.make_opts(prefill_waves=4, phat_scale=hf.PHAT_TILE)]:
+        assert call(o) == 3 and b"prefill_waves" in L.hifa4_last_error()
+    assert call(hf.make_opts(prefill_waves=4), dims=hf.make_dims(1, 4, 2, 256, 64, 64)) == 3
+    stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
+    assert call(hf.make_opts(prefill_waves=4), stats=stats) == 3 and b"statistics" in L.hifa4_last_error()
 
 
 def test_noalloc_rejects_partials_beyond_the_fixed_scratch(L):

@@ -23,9 +23,9 @@ def bench():
     return m
 
 
-PRE = "void hifa4::(anonymous namespace)::attn_prefill_kernel<128, true, 0, false, 0>(hifa4::AttnArgs)"
-D256 = "void hifa4::(anonymous namespace)::attn_prefill_kernel<256, true, 0, false, 0>(hifa4::AttnArgs)"
-DP = "void hifa4::(anonymous namespace)::attn_prefill_kernel<128, true, 0, false, 2>(hifa4::AttnArgs)"
+PRE = "void hifa4::(anonymous namespace)::attn_prefill_kernel<128, true, 0, false, 0, 8>(hifa4::AttnArgs)"
+D256 = "void hifa4::(anonymous namespace)::attn_prefill_kernel<256, true, 0, false, 0, 8>(hifa4::AttnArgs)"
+DP = "void hifa4::(anonymous namespace)::attn_prefill_kernel<128, true, 0, false, 2, 8>(hifa4::AttnArgs)"
 SPLIT = "void hifa4::(anonymous namespace)::attn_decode_split_kernel<128, 0, 0, 2>(hifa4::AttnArgs)"
 MERGE = "void hifa4::(anonymous namespace)::attn_decode_merge_kernel<128>(hifa4::AttnArgs)"
 COPY = "__amd_rocclr_copyBuffer"

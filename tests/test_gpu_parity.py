@@ -11,7 +11,7 @@ import bit_quantized_flashattention_amd as hf
 from oracle import attention as A
 from oracle import mx
 import synth
-from gpu_helpers import compare_out, run_case, gpu_quantize, assert_codes_equal
+from gpu_helpers import compare_out, run_case, gpu_quantize, assert_codes_equal, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +136,34 @@ def test_tiny_and_ragged_shapes(b, hq, hkv, lq, lk, d, causal, kv_tile):
     print("case tiny", b, hq, hkv, lq, lk, d, causal, kv_tile, flush=True)
     got, want, *_ = run_case(q, k, v, causal, kv_tile, calib=cal)
     compare_out(got, want, "tiny-%d-%d-%d" % (lq, lk, d))
+
+
+@pytest.mark.parametrize("b,hq,hkv,lq,lk,d,causal,kv_tile", [
+    (1, 4, 1, 200, 200, 128, True, 128),   # GQA 4: one head group per work-group, ragged rows
+    (2, 2, 2, 150, 150, 128, True, 64),    # MHA: 128 or 64 rows of one head per work-group
+    (1, 16, 1, 70, 70, 128, False, 128),   # GQA 16: 8 or 4 heads per work-group
+    (2, 8, 2, 100, 260, 64, True, 64),     # d = 64, fewer queries than keys (bottom-right causal)
+])
+def test_prefill_work_group_shapes(b, hq, hkv, lq, lk, d, causal, kv_tile):
+    """4- and 8-wave prefill work-groups (opts.prefill_waves) give the same bits as the automatic
+    choice, which matches the oracle bit for bit."""
+    import torch
+    cfg, q, k, v, cal = gen(1, B=b, Hq=hq, Hkv=hkv, Lq=lq, Lk=lk, d=d)
+    print("case work-group shapes", b, hq, hkv, lq, lk, d, causal, kv_tile, flush=True)
+    got, want, *_ = run_case(q, k, v, causal, kv_tile, calib=cal)
+    _, ndiff = compare_out(got, want, "wg-auto")
+    assert ndiff == 0
+    res = gpu_quantize(q, k, v, None, None)
+    dims = hf.make_dims(b, hq, hkv, d, lq, lk)
+    auto = hf.attention_fwd(res, dims, causal, 0, kv_tile)
+    q16 = (to_dev(q), None)
+    kv_only = {n: res[n] for n in ["k_codes", "k_scales", "v_codes", "v_scales"]}
+    for w in (4, 8):
+        o = hf.attention_fwd(res, dims, causal, 0, kv_tile, prefill_waves=w)
+        o16 = hf.attention_fwd(kv_only, dims, causal, 0, kv_tile, q16=q16, prefill_waves=w)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), auto.view(torch.int16)), w
+        assert torch.equal(o16.view(torch.int16), auto.view(torch.int16)), w
 
 
 def test_tile_stats_match_oracle():
