@@ -47,6 +47,10 @@ constexpr int kStatsRows = 16;  // query rows per tile-statistics block (one wav
 #ifndef PREFILL_SMALL_GRID_WAVES
 #define PREFILL_SMALL_GRID_WAVES 4  // waves per work-group of grids too small to fill the chip (0: off)
 #endif
+#ifndef PREFILL_SNAKE
+#define PREFILL_SNAKE 1  // causal small-grid order: alternate direction every 32 work-groups of an XCD
+#endif
+constexpr int kCUsPerXCD = 32;
 constexpr int kStages = PREFILL_STAGES;  // LDS ring depth (2: tile j+1 streams in while j is used)
 
 template <int D, int WAVES = PREFILL_WAVES>
@@ -281,7 +285,21 @@ __global__ __launch_bounds__(WAVES * 64, (MODE == 0 && !STATS && WAVES == PREFIL
   const uint64_t nwg = gx * gy * gridDim.z;
   const uint64_t hwid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const uint64_t per = nwg / 8, rem = nwg % 8, xcd = hwid % 8;
-  const uint64_t lin = xcd * per + (xcd < rem ? xcd : rem) + hwid / 8;
+  uint64_t j = hwid / 8;  // dispatch position inside the XCD's range
+  if constexpr (CAUSAL && PREFILL_SNAKE && WAVES == PREFILL_SMALL_GRID_WAVES) {
+    // A small causal grid is resident all at once, and an XCD deals its work-groups over its 32
+    // compute units in turn, so compute unit c would get positions c, c + 32, ...: with the
+    // heaviest blocks first, the low units would get the heaviest of every round.  Reversing
+    // every other round of 32 gives unit c blocks c, 63 - c, 64 + c, ... of the heaviest-first
+    // order, whose lengths sum about equally.  (A bijection of the XCD's range, checked on the CPU.)
+    const uint64_t n_x = per + (xcd < rem ? 1 : 0);
+    const uint64_t r = j / kCUsPerXCD, c = j % kCUsPerXCD;
+    if (r & 1) {
+      const uint64_t m = n_x - kCUsPerXCD * r < (uint64_t)kCUsPerXCD ? n_x - kCUsPerXCD * r : (uint64_t)kCUsPerXCD;
+      j = kCUsPerXCD * r + (m - 1 - c);
+    }
+  }
+  const uint64_t lin = xcd * per + (xcd < rem ? xcd : rem) + j;
   const uint32_t bx = (uint32_t)(lin % gx), by = (uint32_t)((lin / gx) % gy), bz = (uint32_t)(lin / (gx * gy));
   const int kvh = by / chunks;
   const int h = kvh * group + (by % chunks) * hw + wave / wph;
