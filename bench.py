@@ -8,6 +8,8 @@ forward, which rescales and quantizes its own query rows on the way in
 Hq=32/Hkv=8, d=128, P-Reordered normalizer, P-hat with one scale per 32-key block, 128-key
 tiles).  The JSON line also carries, each with its own roofline:
   prefill_d256       the Gemma2-9B-shaped causal prefill (B=2, L=8192, Hq=16/Hkv=8, d=256);
+  prefill_b1         the Qwen3-8B-shaped single-sequence causal prefill (B=1, L=2048,
+                     Hq=32/Hkv=8, d=128), a grid too small to fill the chip;
   direct_p           the headline workload with Direct-P codes (no exponential per score);
   noncausal          the headline shapes without the causal mask, with the method's codes and
                      with Direct-P codes (the Direct-P page's setting is non-causal inference);
@@ -49,7 +51,7 @@ MIN_WARM_S = 0.3
 COPY_PROBE_BYTES = 512 << 20  # plain device copy run by --traffic-probe to calibrate the counters
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["attn_prefill.hip", "attn_decode.hip", "device_common.h", "quantize.hip"]
-ALL_LEGS = ["prefill_d256", "direct_p", "noncausal", "rope_prefill", "decode"]
+ALL_LEGS = ["prefill_d256", "prefill_b1", "direct_p", "noncausal", "rope_prefill", "decode"]
 
 
 def progress(msg):
@@ -623,6 +625,8 @@ def main():
     }
     if "prefill_d256" in args.leg_list:
         line["prefill_d256"] = bench_prefill(args, 3)[0]
+    if "prefill_b1" in args.leg_list:
+        line["prefill_b1"] = bench_prefill(args, 1)[0]
     if "direct_p" in args.leg_list:
         line["direct_p"] = bench_prefill(args, 2, phat_rule=1)[0]
     if "noncausal" in args.leg_list:
