@@ -10,7 +10,8 @@
 // 16x16x128 scaled FP4 MFMA, so its registers hold one score tile at a time.  A work-group has 8
 // waves; with registers capped at 80 (d <= 128) three work-groups share a CU, 6 waves per SIMD
 // (4 at d = 256), enough for one wave's exponentials to run while another waits on its matrix
-// products or LDS reads.  Tiles are double-buffered in LDS: the next tile is copied from HBM
+// products or LDS reads.  Causal grids that would fill the chip at most once run work-groups of 4
+// waves instead (see launch4).  Tiles are double-buffered in LDS: the next tile is copied from HBM
 // straight into LDS (buffer loads that write LDS) while the current one is computed, so one
 // barrier per tile remains.
 //
