@@ -110,8 +110,8 @@ typedef struct {
   int32_t phat_rule;   /* HIFA4_PHAT_EXP16 (0, the method) or HIFA4_PHAT_DIRECT (1, with
                           HIFA4_PHAT_BLOCK32 only) */
   int32_t prefill_waves; /* prefill work-group size in waves of 16 query rows: 0 = automatic (4 for
-                            causal grids of 8-wave work-groups too small to fill the chip, 8
-                            otherwise), 4 or 8.  4 exists for d <= 128 with HIFA4_P_REORDERED,
+                            causal grids whose 8-wave work-groups would all be resident at once,
+                            at most 768 of them; 8 otherwise), 4 or 8.  4 exists for d <= 128 with HIFA4_P_REORDERED,
                             HIFA4_MAX_CEIL, the method's P-hat and no tile statistics
                             (HIFA4_ERR_UNSUPPORTED otherwise).  Not part of the numerical
                             definition: every wave computes the same rows over the same tiles, so
