@@ -626,10 +626,15 @@ hipError_t launch4(AttnArgs a, hipStream_t s) {
   // no such imbalance and keeps 8 waves, whose K/V tiles serve twice the rows (B1 L2048: 4 waves
   // 45.1 us, 8 waves 42.7 us).  Each wave computes the same 16 rows over the same tiles either
   // way, so the output is bit-identical.  opts.prefill_waves overrides the choice.
-  if constexpr (PREFILL_SMALL_GRID_WAVES > 0 && D <= 128 && MODE == 0 && !STATS && PH == 0) {
+  if constexpr (PREFILL_SMALL_GRID_WAVES > 0 && MODE == 0 && !STATS && PH == 0) {
     AttnArgs big = a;
     const dim3 g = prefill_grid<D, PREFILL_WAVES>(big);
-    const bool small = CAUSAL && (int64_t)g.x * g.y * g.z <= kResidentWorkGroups;
+    // d = 256: LDS holds two work-groups per CU whatever their size, so 4-wave ones halve the
+    // residency of any 8-wave grid with two per CU; they pay only where that grid leaves half the
+    // CUs idle (Hq16/Hkv8: B1 L1024 22.5 -> 20.5 us; B1 L2048, 256 work-groups, even at 36.5-36.9;
+    // B1 L4096 78.5 us with 8 waves, 92.0 with 4)
+    const int64_t limit = D <= 128 ? kResidentWorkGroups : 128;
+    const bool small = CAUSAL && (int64_t)g.x * g.y * g.z <= limit;
     if (a.wg_waves == PREFILL_SMALL_GRID_WAVES || (a.wg_waves == 0 && small)) {
       const dim3 gs = prefill_grid<D, PREFILL_SMALL_GRID_WAVES>(a);
       hipLaunchKernelGGL((attn_prefill_kernel<D, CAUSAL, MODE, STATS, PH, PREFILL_SMALL_GRID_WAVES>), gs,

@@ -111,9 +111,9 @@ hifa4_status check_opts(const hifa4_dims* d, const hifa4_attn_opts* o) {
   if (o->prefill_waves != 0 && o->prefill_waves != 4 && o->prefill_waves != 8)
     return fail(HIFA4_ERR_SHAPE, "prefill_waves must be 0, 4 or 8");
   if (o->prefill_waves == 4 && d->len_q > 1 &&
-      (d->head_dim > 128 || o->normalizer != HIFA4_P_REORDERED || o->max_rule != HIFA4_MAX_CEIL ||
+      (o->normalizer != HIFA4_P_REORDERED || o->max_rule != HIFA4_MAX_CEIL ||
        o->phat_rule != HIFA4_PHAT_EXP16 || o->phat_scale != HIFA4_PHAT_BLOCK32))
-    return fail(HIFA4_ERR_UNSUPPORTED, "prefill_waves = 4 runs d <= 128 with the method's P-Reordered rules only");
+    return fail(HIFA4_ERR_UNSUPPORTED, "prefill_waves = 4 runs the method's P-Reordered rules only");
   if (o->causal && d->len_q > d->len_kv) return fail(HIFA4_ERR_SHAPE, "causal attention needs len_q <= len_kv");
   if (o->kv_capacity != 0 &&
       (o->kv_capacity < d->len_kv || round32(o->kv_capacity) * (d->head_dim / 2) >= (int64_t(1) << 31)))

@@ -110,12 +110,11 @@ typedef struct {
   int32_t phat_rule;   /* HIFA4_PHAT_EXP16 (0, the method) or HIFA4_PHAT_DIRECT (1, with
                           HIFA4_PHAT_BLOCK32 only) */
   int32_t prefill_waves; /* prefill work-group size in waves of 16 query rows: 0 = automatic (4 for
-                            causal grids whose 8-wave work-groups would all be resident at once,
-                            at most 768 of them; 8 otherwise), 4 or 8.  4 exists for d <= 128 with HIFA4_P_REORDERED,
-                            HIFA4_MAX_CEIL, the method's P-hat and no tile statistics
-                            (HIFA4_ERR_UNSUPPORTED otherwise).  Not part of the numerical
-                            definition: every wave computes the same rows over the same tiles, so
-                            the output is bit-identical.  Decode ignores it. */
+                            causal grids of at most 768 8-wave work-groups at d <= 128, all
+                            resident at once, or at most 128 at d = 256; 8 otherwise), 4 or 8.  4 exists for HIFA4_P_REORDERED, HIFA4_MAX_CEIL, the method's P-hat
+                            and no tile statistics (HIFA4_ERR_UNSUPPORTED otherwise).  Not part of
+                            the numerical definition: every wave computes the same rows over the
+                            same tiles, so the output is bit-identical.  Decode ignores it. */
 } hifa4_attn_opts;
 
 /*

@@ -147,13 +147,12 @@ def test_prefill_waves_is_validated(L):
         return L.hifa4_attention_fwd(ctypes.byref(dims), ctypes.byref(o), *([dummy] * 7), None, 0, stats, None)
     for w in (1, 2, 6, 16, -4):
         assert call(hf.make_opts(prefill_waves=w)) == 2 and b"prefill_waves" in L.hifa4_last_error()
-    # 4-wave work-groups exist for the method's P-Reordered instance at d <= 128 only
+    # 4-wave work-groups exist for the method's P-Reordered instance only
     for o in [hf.make_opts(prefill_waves=4, normalizer=hf.INCONSISTENT),
               hf.make_opts(prefill_waves=4, max_rule=hf.MAX_NEAREST16),
               hf.make_opts(prefill_waves=4, phat_rule=hf.PHAT_DIRECT),
               hf.make_opts(prefill_waves=4, phat_scale=hf.PHAT_TILE)]:
         assert call(o) == 3 and b"prefill_waves" in L.hifa4_last_error()
-    assert call(hf.make_opts(prefill_waves=4), dims=hf.make_dims(1, 4, 2, 256, 64, 64)) == 3
     stats = ctypes.cast(dummy, ctypes.POINTER(ctypes.c_float))
     assert call(hf.make_opts(prefill_waves=4), stats=stats) == 3 and b"statistics" in L.hifa4_last_error()
 

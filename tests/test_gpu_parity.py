@@ -143,6 +143,7 @@ def test_tiny_and_ragged_shapes(b, hq, hkv, lq, lk, d, causal, kv_tile):
     (2, 2, 2, 150, 150, 128, True, 64),    # MHA: 128 or 64 rows of one head per work-group
     (1, 16, 1, 70, 70, 128, False, 128),   # GQA 16: 8 or 4 heads per work-group
     (2, 8, 2, 100, 260, 64, True, 64),     # d = 64, fewer queries than keys (bottom-right causal)
+    (1, 4, 2, 150, 150, 256, True, 128),   # d = 256, GQA 2
 ])
 def test_prefill_work_group_shapes(b, hq, hkv, lq, lk, d, causal, kv_tile):
     """4- and 8-wave prefill work-groups (opts.prefill_waves) give the same bits as the automatic
